@@ -1,0 +1,335 @@
+"""Benchmark of the heterogeneous sliding-window attention path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload c2_decode]
+                    [--prefill-workload c1_prefill] [--no-cpu-baseline]
+
+A step is one decode step of the whole batch: the new token's K/V appended
+to every head's ring (moa_kv_append, n_new = 1), then split-K decode
+attention over the rings (moa_decode, one kernel).  The default workload is
+the Vicuna-7B-shaped decode (B64, H32, D128, prompt 16384, 50 % mean
+density); `value` is decode tokens/s of that batch (B tokens per step) with
+every input resident in HBM.  The same run times the Vicuna-7B-shaped
+prefill (B1, H32, D128, N8192) and reports its TFLOP/s over the kept
+(query, key) pairs only.
+
+Rooflines: the decode kernel against 8 TB/s HBM (algorithmic bytes: K and V
+ring reads, q read, o write), the prefill kernel against 2.5 PFLOP/s dense
+bf16 MFMA (4*D flops per kept pair).  Kernel durations come from HIP events
+recorded on the launch stream around every launch in the timed region.
+
+The CPU baseline times the oracle (oracle/, float64 numpy) on a bounded
+sample of the same workload on this host; it is a reported baseline only.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("decode attn tokens/s + HBM GB/s % peak; prefill TFLOP/s % MFMA peak")
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "decode_c2_counters.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kept_pairs(s, n):
+    """Kept (query, key) pairs of one head with span s over n rows."""
+    s = min(int(s), int(n))
+    return n * s - s * (s - 1) // 2
+
+
+def prefill_flops(plan):
+    g = plan.n_q_heads // plan.n_kv_heads
+    pairs = sum(kept_pairs(plan.spans[h // g], plan.n_prompt) for h in range(plan.n_q_heads))
+    return 4.0 * plan.head_dim * plan.batch * pairs
+
+
+def decode_kernel_bytes(plan):
+    """K and V ring reads plus q read and o write, bf16."""
+    d, b = plan.head_dim, plan.batch
+    return 2 * 2 * d * b * int(plan.slots_per_seq) + 2 * 2 * d * b * plan.n_q_heads
+
+
+def append_bytes(plan):
+    """New K and V rows read and written once, bf16."""
+    return 2 * 2 * 2 * plan.head_dim * plan.batch * plan.n_kv_heads
+
+
+def src_sha(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "heterogeneous_sliding_windows_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic():
+    """Per-launch HBM bytes of the decode kernel from committed counter runs, or None
+    when the kernel sources changed since the counters were taken."""
+    try:
+        with open(PROFILE_COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("src_sha") != src_sha("decode.hip", "moa_device.h"):
+        return None
+    return c.get("traffic_bytes_per_launch")
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return os.cpu_count()
+
+
+# ---------------------------------------------------------------------------
+# GPU legs
+# ---------------------------------------------------------------------------
+
+def run_decode(moa, workloads, torch, name, steps, warmup):
+    w = workloads.WORKLOADS[name]
+    alpha, beta = workloads.rules(name)
+    plan = moa.Plan(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, alpha, beta)
+    log(f"{name}: rings {2 * plan.cache_elems * 2 / 1e9:.2f} GB, {plan.decode_chunks().shape[0]}"
+        f" chunks/seq, workspace {plan.workspace_bytes / 1e6:.1f} MB")
+    dev = torch.device("cuda")
+    kc = workloads.device_normal_(torch.empty(plan.cache_elems, dtype=torch.bfloat16, device=dev), 11)
+    vc = workloads.device_normal_(torch.empty(plan.cache_elems, dtype=torch.bfloat16, device=dev), 12)
+    ws = plan.new_workspace()
+    total = warmup + steps
+    qs = workloads.device_normal_(torch.empty(total, w.batch, w.n_q_heads, w.head_dim,
+                                              dtype=torch.bfloat16, device=dev), 13)
+    ks = workloads.device_normal_(torch.empty(total, w.batch, w.n_kv_heads, 1, w.head_dim,
+                                              dtype=torch.bfloat16, device=dev), 14)
+    vs = workloads.device_normal_(torch.empty(total, w.batch, w.n_kv_heads, 1, w.head_dim,
+                                              dtype=torch.bfloat16, device=dev), 15)
+    out = torch.empty(w.batch, w.n_q_heads, w.head_dim, dtype=torch.bfloat16, device=dev)
+    n = w.n_prompt
+    stream = torch.cuda.current_stream()
+
+    def step(t):
+        plan.kv_append(kc, vc, ks[t], vs[t], n + t, stream=stream)
+        plan.decode(qs[t], kc, vc, n + t, out, ws, stream=stream)
+
+    for t in range(warmup):
+        step(t)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(steps):
+        t = warmup + i
+        plan.kv_append(kc, vc, ks[t], vs[t], n + t, stream=stream)
+        ev[i][0].record(stream)
+        plan.decode(qs[t], kc, vc, n + t, out, ws, stream=stream)
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    elapsed_ms = t_start.elapsed_time(t_end)
+    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    assert torch.isfinite(out.float()).all(), "non-finite decode output"
+    res = dict(plan=plan, elapsed_ms=elapsed_ms, decode_ms=dec_ms, w=w)
+    del kc, vc, ws, qs, ks, vs
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_prefill(moa, workloads, torch, name, iters, warmup):
+    w = workloads.WORKLOADS[name]
+    alpha, beta = workloads.rules(name)
+    plan = moa.Plan(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, alpha, beta)
+    dev = torch.device("cuda")
+    shp_q = (w.batch, w.n_q_heads, w.n_prompt, w.head_dim)
+    shp_kv = (w.batch, w.n_kv_heads, w.n_prompt, w.head_dim)
+    q = workloads.device_normal_(torch.empty(shp_q, dtype=torch.bfloat16, device=dev), 21)
+    k = workloads.device_normal_(torch.empty(shp_kv, dtype=torch.bfloat16, device=dev), 22)
+    v = workloads.device_normal_(torch.empty(shp_kv, dtype=torch.bfloat16, device=dev), 23)
+    o = torch.empty_like(q)
+    kc, vc = plan.new_cache()
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        plan.prefill(q, k, v, o, stream=stream)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(iters)]
+    for a, b in ev:
+        a.record(stream)
+        plan.prefill(q, k, v, o, stream=stream)
+        b.record(stream)
+    h0, h1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    h0.record(stream)
+    plan.kv_append(kc, vc, k, v, 0, stream=stream)       # prompt -> ring handoff
+    h1.record(stream)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all(), "non-finite prefill output"
+    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    res = dict(plan=plan, ms=ms, handoff_ms=h0.elapsed_time(h1), w=w)
+    del q, k, v, o, kc, vc
+    torch.cuda.empty_cache()
+    return res
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline legs (the oracle as it stands)
+# ---------------------------------------------------------------------------
+
+def cpu_baseline_decode(plan, budget_s):
+    import oracle
+    rng = np.random.Generator(np.random.PCG64(31))
+    d, g, n = plan.head_dim, plan.n_q_heads // plan.n_kv_heads, plan.n_prompt
+    hist = []
+    for h in range(plan.n_kv_heads):
+        s = int(plan.spans[h])
+        pos = np.arange(n - s + 1, n + 1)
+        hist.append((rng.standard_normal((s, d), dtype=np.float32),
+                     rng.standard_normal((s, d), dtype=np.float32), pos, s))
+    q = rng.standard_normal((plan.n_q_heads, d), dtype=np.float32)
+    tokens = 0
+    t0 = time.perf_counter()
+    while True:
+        for h, (hk, hv, pos, s) in enumerate(hist):
+            oracle.decode_step(q[h * g:(h + 1) * g], hk, hv, pos, n, s)
+        tokens += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": tokens / el, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{tokens} decode tokens (one sequence each, all {plan.n_kv_heads} KV heads, "
+                      f"full rings) in {el:.1f} s, float64 numpy"}
+
+
+def cpu_baseline_prefill(plan, budget_s):
+    import oracle
+    rng = np.random.Generator(np.random.PCG64(32))
+    d, n, g = plan.head_dim, plan.n_prompt, plan.n_q_heads // plan.n_kv_heads
+    k = rng.standard_normal((n, d), dtype=np.float32)
+    v = rng.standard_normal((n, d), dtype=np.float32)
+    flops, rows_done = 0.0, 0
+    t0 = time.perf_counter()
+    h = 0
+    while True:
+        s = int(plan.spans[(h % plan.n_q_heads) // g])
+        rows = [int(x) for x in rng.integers(0, n, 16)]
+        oracle.prefill_rows(rng.standard_normal((16, d), dtype=np.float32), k, v, s, rows)
+        flops += sum(4.0 * d * min(r + 1, s) for r in rows)
+        rows_done += 16
+        h += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": f"{rows_done} random query rows over the heads' spans in {el:.1f} s, "
+                      f"float64 numpy"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", default="c2_decode")
+    ap.add_argument("--prefill-workload", default="c1_prefill")
+    ap.add_argument("--prefill-iters", type=int, default=20)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the attention path has "
+              "no cross-GPU step here; see DESIGN.md for how it would shard.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import heterogeneous_sliding_windows_amd as moa
+    import workloads
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    log(f"decode workload {args.workload}: warmup {args.warmup}, steps {args.steps}")
+    dres = run_decode(moa, workloads, torch, args.workload, args.steps, args.warmup)
+    plan, w = dres["plan"], dres["w"]
+    ms_step = dres["elapsed_ms"] / args.steps
+    tokens_s = w.batch * args.steps / (dres["elapsed_ms"] / 1e3)
+    kbytes = decode_kernel_bytes(plan)
+    step_bytes = kbytes + append_bytes(plan)
+    achieved = kbytes / (dres["decode_ms"] / 1e3) / 1e9
+    log(f"decode: {ms_step:.3f} ms/step, kernel {dres['decode_ms']:.3f} ms, "
+        f"{achieved:.0f} GB/s, {tokens_s:.0f} tokens/s")
+
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) bf16 q/k/v and rings, seeded per-head rules "
+                "(tests/golden/rules.json)",
+        "config": {"workload": f"{w.name}: {w.title}", "batch": w.batch,
+                   "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                   "head_dim": w.head_dim, "n_prompt": w.n_prompt,
+                   "mean_density": round(float(np.mean(plan.spans)) / w.n_prompt, 4),
+                   "step": "kv_append(1 token/seq) + decode, one layer"},
+        "hbm": {"step_GBps": round(step_bytes / (ms_step / 1e3) / 1e9, 1),
+                "step_frac": round(step_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+                "bytes_per_step": step_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": counter_traffic(), "kernel": f"decode_kernel<{w.head_dim}>",
+                     "algorithmic_bytes_per_launch": kbytes,
+                     "avg_launch_ms": round(dres["decode_ms"], 4)},
+    }
+
+    if not args.no_prefill:
+        log(f"prefill workload {args.prefill_workload}")
+        pres = run_prefill(moa, workloads, torch, args.prefill_workload, args.prefill_iters, 3)
+        pplan, pw = pres["plan"], pres["w"]
+        fl = prefill_flops(pplan)
+        tf = fl / (pres["ms"] / 1e3) / 1e12
+        log(f"prefill: {pres['ms']:.3f} ms, {tf:.1f} TFLOP/s, handoff {pres['handoff_ms']:.3f} ms")
+        line["prefill"] = {
+            "workload": f"{pw.name}: {pw.title}", "ms": round(pres["ms"], 4),
+            "tflops": round(tf, 2), "handoff_ms": round(pres["handoff_ms"], 4),
+            "flops": fl,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": None, "kernel": f"prefill_bf16_kernel<{pw.head_dim}>"},
+        }
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        line["cpu_baseline"] = cpu_baseline_decode(plan, args.cpu_budget)
+        if not args.no_prefill:
+            line["prefill"]["cpu_baseline"] = cpu_baseline_prefill(pplan, args.cpu_budget / 2)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

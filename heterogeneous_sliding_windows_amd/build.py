@@ -1,0 +1,73 @@
+"""Build libmoa.so (gfx950) in the package directory with hipcc.
+
+    python -m heterogeneous_sliding_windows_amd.build [-v]
+
+Every call recompiles all sources.  Objects go to _build/ at the repository
+root; the shared library lands next to this file, where the binding loads it.
+"""
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libmoa.so")
+ARCH = "gfx950"
+
+SOURCES = ["moa_abi.cpp", "prefill.hip", "kv_append.hip", "decode.hip"]
+
+COMMON = [
+    "--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
+    "-I", os.path.join(ROOT, "include"),
+    # no packed fp32 instructions: they are kept out of every kernel
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+# per-source extra flags: the span table needs IEEE double with no contraction
+EXTRA = {"moa_abi.cpp": ["-ffp-contract=off"]}
+
+
+def hipcc():
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libmoa)")
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    out = (r.stdout + r.stderr).strip()
+    # the host pass does not know the packed-fp32 feature; that note is harmless
+    lines = [ln for ln in out.splitlines() if "packed-fp32-ops" not in ln]
+    if r.returncode != 0:
+        raise RuntimeError("build failed:\n" + " ".join(cmd) + "\n" + "\n".join(lines))
+    if verbose and lines:
+        print("\n".join(lines))
+
+
+def build(verbose=False):
+    cc = hipcc()
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD, src + ".o")
+        cmd = [cc, *COMMON, *EXTRA.get(src, []), "-x", "hip", "-c",
+               os.path.join(CSRC, src), "-o", obj]
+        jobs.append((cmd, obj))
+    with ThreadPoolExecutor(max_workers=min(len(jobs), 4)) as ex:
+        list(ex.map(lambda j: _run(j[0], verbose), jobs))
+    tmp = LIB + ".tmp"
+    _run([cc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *[o for _, o in jobs]],
+         verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

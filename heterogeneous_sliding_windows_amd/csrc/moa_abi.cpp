@@ -1,0 +1,370 @@
+// C ABI of libmoa: argument checks, the host planner (span table, ring
+// offsets, prefill tile list, decode chunk list) and kernel dispatch.
+//
+// Built with -ffp-contract=off so that alpha + beta * N is evaluated with one
+// rounding per operation, as the span table's definition requires.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "moa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MOA_EHIP, "%s failed: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+constexpr int64_t kMaxN = (int64_t)1 << 31;
+
+// Span of one head (project page, "Finding 2" and "Elastic search space"):
+// clamp(64 * ceil(x / 64), 1, N) with x = alpha + beta * N in IEEE double.
+#pragma clang fp contract(off)
+int32_t span_of(int64_t alpha, double beta, int64_t n) {
+  const double x = (double)alpha + beta * (double)n;
+  if (!(x > 0.0)) return 1;                    // x <= 0: the query alone
+  if (x >= (double)n) return (int32_t)n;       // saturated
+  const double r = 64.0 * std::ceil(x / 64.0);  // exact: x < 2^31
+  int64_t s = (int64_t)r;
+  if (s < 1) s = 1;
+  if (s > n) s = n;
+  return (int32_t)s;
+}
+
+int check_rules(const int64_t* alpha, const double* beta, int32_t hkv, int64_t n) {
+  if (!alpha || !beta) return fail(MOA_EINVAL, "alpha and beta must not be NULL");
+  if (hkv < 1) return fail(MOA_EINVAL, "n_kv_heads must be >= 1 (got %d)", hkv);
+  if (n < 1 || n >= kMaxN) return fail(MOA_EINVAL, "n_prompt must be in [1, 2^31) (got %lld)", (long long)n);
+  for (int32_t h = 0; h < hkv; ++h) {
+    if (alpha[h] < 0) return fail(MOA_EINVAL, "alpha[%d] = %lld is negative", h, (long long)alpha[h]);
+    if (!std::isfinite(beta[h]) || beta[h] < 0.0)
+      return fail(MOA_EINVAL, "beta[%d] = %g must be finite and >= 0", h, beta[h]);
+  }
+  return MOA_OK;
+}
+
+template <class T>
+int dev_upload(T** dst, const std::vector<T>& src) {
+  *dst = nullptr;
+  if (src.empty()) return MOA_OK;
+  hipError_t e = hipMalloc((void**)dst, src.size() * sizeof(T));
+  if (e != hipSuccess) {
+    *dst = nullptr;
+    return e == hipErrorOutOfMemory ? fail(MOA_ENOMEM, "hipMalloc of plan tables: out of memory")
+                                    : hip_fail(e, "hipMalloc (plan tables)");
+  }
+  e = hipMemcpy(*dst, src.data(), src.size() * sizeof(T), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy (plan tables)");
+  return MOA_OK;
+}
+
+void free_device(moa_plan* p) {
+  hipFree(p->dev.span);
+  hipFree(p->dev.offset);
+  hipFree(p->dev.prefill_items);
+  hipFree(p->dev.decode_chunks);
+  hipFree(p->dev.head_chunks);
+  p->dev = moa::PlanDevice{};
+}
+
+// Prefill work list: every (b, h_q, 128-row query tile) with the range of
+// 64-key tiles holding at least one kept pair.  The union of the windows of
+// rows i0..i1 is the contiguous key range [max(0, i0 - S + 1), i1], so the
+// live tiles form one range.  Sorted by tile count (longest first, so the
+// tail of the launch holds the short items), ties in (bh, q_tile) order.
+void build_prefill_items(moa_plan* p) {
+  const int64_t n_qt = (p->N + moa::kPrefillBM - 1) / moa::kPrefillBM;
+  struct Item { int32_t bh, qt, lo, hi; };
+  std::vector<Item> items;
+  items.reserve((size_t)p->B * p->Hq * n_qt);
+  for (int32_t b = 0; b < p->B; ++b)
+    for (int32_t h = 0; h < p->Hq; ++h) {
+      const int64_t s = p->span[h / p->G];
+      for (int64_t qt = 0; qt < n_qt; ++qt) {
+        const int64_t i0 = qt * moa::kPrefillBM;
+        const int64_t i1 = std::min<int64_t>(i0 + moa::kPrefillBM, p->N) - 1;
+        const int64_t j0 = std::max<int64_t>(0, i0 - s + 1);
+        items.push_back({b * p->Hq + h, (int32_t)qt, (int32_t)(j0 / moa::kPrefillBN),
+                         (int32_t)(i1 / moa::kPrefillBN)});
+      }
+    }
+  std::stable_sort(items.begin(), items.end(), [](const Item& a, const Item& b) {
+    return (a.hi - a.lo) > (b.hi - b.lo);
+  });
+  p->prefill_items.resize(items.size() * 4);
+  for (size_t i = 0; i < items.size(); ++i) {
+    p->prefill_items[4 * i + 0] = items[i].bh;
+    p->prefill_items[4 * i + 1] = items[i].qt;
+    p->prefill_items[4 * i + 2] = items[i].lo;
+    p->prefill_items[4 * i + 3] = items[i].hi;
+  }
+}
+
+// Decode chunk list of one sequence: each head's S_h slots cut into chunks
+// of at most decode_chunk slots, heads in order.
+void build_decode_chunks(moa_plan* p) {
+  const int32_t c = p->decode_chunk;
+  p->decode_chunks.clear();
+  p->head_chunks.assign((size_t)p->Hkv * 2, 0);
+  int32_t idx = 0;
+  for (int32_t h = 0; h < p->Hkv; ++h) {
+    const int32_t s = p->span[h];
+    const int32_t cnt = (s + c - 1) / c;
+    p->head_chunks[2 * h + 0] = idx;
+    p->head_chunks[2 * h + 1] = cnt;
+    for (int32_t k = 0; k < cnt; ++k) {
+      p->decode_chunks.push_back(h);
+      p->decode_chunks.push_back(k * c);
+      p->decode_chunks.push_back(std::min(c, s - k * c));
+      p->decode_chunks.push_back(cnt);
+      ++idx;
+    }
+  }
+  p->n_chunks = idx;
+}
+
+int check_plan(moa_plan_t p, bool need_device) {
+  if (!p) return fail(MOA_EINVAL, "plan is NULL");
+  if (need_device && p->host_only)
+    return fail(MOA_EINVAL, "plan was created with MOA_PLAN_HOST_ONLY; no device tables");
+  return MOA_OK;
+}
+
+int set_device(const moa_plan* p) {
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (cur != p->device)
+    return fail(MOA_EINVAL, "plan was created on device %d but device %d is current", p->device, cur);
+  return MOA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moa_spans(const int64_t* alpha, const double* beta, int32_t n_kv_heads, int64_t n_prompt,
+              int32_t* span) {
+  int st = check_rules(alpha, beta, n_kv_heads, n_prompt);
+  if (st != MOA_OK) return st;
+  if (!span) return fail(MOA_EINVAL, "span output must not be NULL");
+  for (int32_t h = 0; h < n_kv_heads; ++h) span[h] = span_of(alpha[h], beta[h], n_prompt);
+  return MOA_OK;
+}
+
+int moa_ring_offsets(const int32_t* span, int32_t n_kv_heads, int64_t* offset,
+                     int64_t* slots_per_seq) {
+  if (!span || !offset || !slots_per_seq) return fail(MOA_EINVAL, "NULL argument to moa_ring_offsets");
+  if (n_kv_heads < 1) return fail(MOA_EINVAL, "n_kv_heads must be >= 1 (got %d)", n_kv_heads);
+  int64_t total = 0;
+  for (int32_t h = 0; h < n_kv_heads; ++h) {
+    if (span[h] < 1) return fail(MOA_EINVAL, "span[%d] = %d must be >= 1", h, span[h]);
+    offset[h] = total;
+    total += span[h];
+  }
+  *slots_per_seq = total;
+  return MOA_OK;
+}
+
+int moa_plan_create(const moa_problem* pr, uint32_t flags, moa_plan_t* out) {
+  if (!out) return fail(MOA_EINVAL, "out must not be NULL");
+  *out = nullptr;
+  if (!pr) return fail(MOA_EINVAL, "problem must not be NULL");
+  if (flags & ~MOA_PLAN_HOST_ONLY) return fail(MOA_EINVAL, "unknown flags 0x%x", flags);
+  if (pr->batch < 1) return fail(MOA_EINVAL, "batch must be >= 1 (got %d)", pr->batch);
+  if (pr->n_q_heads < 1) return fail(MOA_EINVAL, "n_q_heads must be >= 1 (got %d)", pr->n_q_heads);
+  int st = check_rules(pr->alpha, pr->beta, pr->n_kv_heads, pr->n_prompt);
+  if (st != MOA_OK) return st;
+  if (pr->n_q_heads % pr->n_kv_heads)
+    return fail(MOA_EINVAL, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)", pr->n_q_heads,
+                pr->n_kv_heads);
+  if (pr->n_q_heads / pr->n_kv_heads > 16)
+    return fail(MOA_EUNSUPPORTED, "query heads per KV head must be <= 16 (got %d)",
+                pr->n_q_heads / pr->n_kv_heads);
+  if (pr->head_dim != 64 && pr->head_dim != 128)
+    return fail(MOA_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", pr->head_dim);
+  if (pr->dtype != MOA_F32 && pr->dtype != MOA_BF16)
+    return fail(MOA_EUNSUPPORTED, "unknown dtype %d", pr->dtype);
+  // Every element index of the largest tensor must fit int64 comfortably and
+  // the per-launch item counts must fit int32 grids.
+  const double elems = (double)pr->batch * pr->n_q_heads * (double)pr->n_prompt * pr->head_dim;
+  if (elems > 9.0e15) return fail(MOA_EINVAL, "problem too large");
+  const double items = (double)pr->batch * pr->n_q_heads *
+                       ((pr->n_prompt + moa::kPrefillBM - 1) / moa::kPrefillBM);
+  if (items > 2.0e9) return fail(MOA_EINVAL, "too many prefill tiles for one launch");
+
+  moa_plan* p = new (std::nothrow) moa_plan;
+  if (!p) return fail(MOA_ENOMEM, "host allocation of the plan failed");
+  try {
+    p->B = pr->batch;
+    p->Hq = pr->n_q_heads;
+    p->Hkv = pr->n_kv_heads;
+    p->G = pr->n_q_heads / pr->n_kv_heads;
+    p->D = pr->head_dim;
+    p->N = pr->n_prompt;
+    p->dtype = pr->dtype;
+    p->host_only = (flags & MOA_PLAN_HOST_ONLY) != 0;
+    p->span.resize(p->Hkv);
+    p->offset.resize(p->Hkv);
+    for (int32_t h = 0; h < p->Hkv; ++h) p->span[h] = span_of(pr->alpha[h], pr->beta[h], p->N);
+    moa_ring_offsets(p->span.data(), p->Hkv, p->offset.data(), &p->slots);
+    build_prefill_items(p);
+    build_decode_chunks(p);
+    if ((double)p->B * (double)p->n_chunks > 2.0e9) {
+      delete p;
+      return fail(MOA_EINVAL, "too many decode chunks for one launch");
+    }
+  } catch (const std::bad_alloc&) {
+    delete p;
+    return fail(MOA_ENOMEM, "host allocation of plan tables failed");
+  }
+
+  if (!p->host_only) {
+    hipError_t e = hipGetDevice(&p->device);
+    if (e != hipSuccess) {
+      delete p;
+      return hip_fail(e, "hipGetDevice");
+    }
+    std::vector<int4> items(p->prefill_items.size() / 4), chunks(p->decode_chunks.size() / 4);
+    std::vector<int2> hc(p->Hkv);
+    std::memcpy(items.data(), p->prefill_items.data(), p->prefill_items.size() * 4);
+    std::memcpy(chunks.data(), p->decode_chunks.data(), p->decode_chunks.size() * 4);
+    std::memcpy(hc.data(), p->head_chunks.data(), p->head_chunks.size() * 4);
+    if ((st = dev_upload(&p->dev.span, p->span)) != MOA_OK ||
+        (st = dev_upload(&p->dev.offset, p->offset)) != MOA_OK ||
+        (st = dev_upload(&p->dev.prefill_items, items)) != MOA_OK ||
+        (st = dev_upload(&p->dev.decode_chunks, chunks)) != MOA_OK ||
+        (st = dev_upload(&p->dev.head_chunks, hc)) != MOA_OK) {
+      free_device(p);
+      delete p;
+      return st;
+    }
+  }
+  *out = p;
+  return MOA_OK;
+}
+
+int moa_plan_destroy(moa_plan_t p) {
+  if (!p) return MOA_OK;
+  if (!p->host_only) free_device(p);
+  delete p;
+  return MOA_OK;
+}
+
+int moa_plan_tables(moa_plan_t p, int32_t* span, int64_t* offset, int64_t* slots_per_seq) {
+  int st = check_plan(p, false);
+  if (st != MOA_OK) return st;
+  if (span) std::copy(p->span.begin(), p->span.end(), span);
+  if (offset) std::copy(p->offset.begin(), p->offset.end(), offset);
+  if (slots_per_seq) *slots_per_seq = p->slots;
+  return MOA_OK;
+}
+
+int64_t moa_cache_elems(moa_plan_t p) {
+  if (check_plan(p, false) != MOA_OK) return 0;
+  return (int64_t)p->B * p->slots * p->D;
+}
+
+size_t moa_decode_workspace_bytes(moa_plan_t p) {
+  if (check_plan(p, false) != MOA_OK) return 0;
+  return moa::decode_ws_bytes(*p);
+}
+
+int64_t moa_plan_prefill_items(moa_plan_t p, int32_t* out) {
+  int st = check_plan(p, false);
+  if (st != MOA_OK) return st;
+  if (out) std::copy(p->prefill_items.begin(), p->prefill_items.end(), out);
+  return (int64_t)(p->prefill_items.size() / 4);
+}
+
+int64_t moa_plan_decode_chunks(moa_plan_t p, int32_t* out) {
+  int st = check_plan(p, false);
+  if (st != MOA_OK) return st;
+  const size_t n = p->decode_chunks.size() / 4;
+  if (out)
+    for (size_t i = 0; i < n; ++i) {
+      out[3 * i + 0] = p->decode_chunks[4 * i + 0];
+      out[3 * i + 1] = p->decode_chunks[4 * i + 1];
+      out[3 * i + 2] = p->decode_chunks[4 * i + 2];
+    }
+  return (int64_t)n;
+}
+
+int32_t moa_plan_decode_chunk(moa_plan_t p) {
+  int st = check_plan(p, false);
+  if (st != MOA_OK) return st;
+  return p->decode_chunk;
+}
+
+int moa_prefill(moa_plan_t p, const void* q, const void* k, const void* v, void* o, void* stream) {
+  int st = check_plan(p, true);
+  if (st != MOA_OK) return st;
+  if (!q || !k || !v || !o) return fail(MOA_EINVAL, "moa_prefill: q, k, v and o must not be NULL");
+  if ((st = set_device(p)) != MOA_OK) return st;
+  hipError_t e = p->dtype == MOA_BF16
+                     ? moa::launch_prefill_bf16(*p, q, k, v, o, (hipStream_t)stream)
+                     : moa::launch_prefill_f32(*p, q, k, v, o, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return MOA_OK;
+}
+
+int moa_kv_append(moa_plan_t p, void* kc, void* vc, const void* kn, const void* vn, int64_t pos0,
+                  int64_t n_new, void* stream) {
+  int st = check_plan(p, true);
+  if (st != MOA_OK) return st;
+  if (!kc || !vc || !kn || !vn)
+    return fail(MOA_EINVAL, "moa_kv_append: caches and new rows must not be NULL");
+  if (pos0 < 0) return fail(MOA_EINVAL, "moa_kv_append: pos0 must be >= 0 (got %lld)", (long long)pos0);
+  if (n_new < 1) return fail(MOA_EINVAL, "moa_kv_append: n_new must be >= 1 (got %lld)", (long long)n_new);
+  if (n_new >= kMaxN || pos0 > ((int64_t)1 << 62) - n_new)
+    return fail(MOA_EINVAL, "moa_kv_append: positions out of range");
+  if ((st = set_device(p)) != MOA_OK) return st;
+  hipError_t e = moa::launch_kv_append(*p, kc, vc, kn, vn, pos0, n_new, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "kv_append launch");
+  return MOA_OK;
+}
+
+int moa_decode(moa_plan_t p, const void* q, const void* kc, const void* vc, int64_t pos, void* o,
+               void* ws, size_t ws_bytes, void* stream) {
+  int st = check_plan(p, true);
+  if (st != MOA_OK) return st;
+  if (!q || !kc || !vc || !o || !ws)
+    return fail(MOA_EINVAL, "moa_decode: q, caches, o and workspace must not be NULL");
+  if (pos < p->N)
+    return fail(MOA_EINVAL, "moa_decode: pos (%lld) must be >= the prompt length %lld", (long long)pos,
+                (long long)p->N);
+  if (p->dtype != MOA_BF16) return fail(MOA_EUNSUPPORTED, "moa_decode supports bfloat16 plans only");
+  const size_t need = moa::decode_ws_bytes(*p);
+  if (ws_bytes < need)
+    return fail(MOA_EWORKSPACE, "moa_decode: workspace of %zu bytes, %zu needed", ws_bytes, need);
+  if ((st = set_device(p)) != MOA_OK) return st;
+  hipError_t e = moa::launch_decode_bf16(*p, q, kc, vc, o, ws, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return MOA_OK;
+}
+
+const char* moa_last_error(void) { return g_last_error.c_str(); }
+
+const char* moa_version(void) { return "libmoa 0.1 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+// Internal declarations shared by the C ABI (moa_abi.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <vector>
+
+#include "../../include/moa.h"
+
+namespace moa {
+
+// Prefill tiling: a work item is 128 query rows of one (b, h_q); keys are
+// streamed in tiles of 64.  Both are fixed by the kernels.
+constexpr int kPrefillBM = 128;
+constexpr int kPrefillBN = 64;
+// Default decode chunk (slots of one head's ring per workgroup).
+constexpr int kDecodeChunk = 1024;
+
+struct PlanDevice {
+  int32_t* span = nullptr;          // [Hkv]
+  int64_t* offset = nullptr;        // [Hkv]
+  int4* prefill_items = nullptr;    // [n_prefill_items] {bh, q_tile, kt_lo, kt_hi}
+  int4* decode_chunks = nullptr;    // [n_chunks] {h_kv, first_slot, n_slots, chunks_of_head}
+  int2* head_chunks = nullptr;      // [Hkv] {first chunk index, chunk count}
+};
+
+}  // namespace moa
+
+struct moa_plan {
+  int32_t B = 0, Hq = 0, Hkv = 0, D = 0, G = 0, dtype = 0;
+  int64_t N = 0;
+  bool host_only = false;
+  int device = -1;
+  std::vector<int32_t> span;
+  std::vector<int64_t> offset;
+  int64_t slots = 0;                      // slots per sequence = sum of spans
+  std::vector<int32_t> prefill_items;     // 4 per item
+  std::vector<int32_t> decode_chunks;     // 4 per chunk (h, first, n, chunks_of_head)
+  std::vector<int32_t> head_chunks;       // 2 per KV head (first, count)
+  int32_t decode_chunk = moa::kDecodeChunk;
+  int64_t n_chunks = 0;                   // chunks per sequence
+  moa::PlanDevice dev;
+};
+
+namespace moa {
+
+// Kernel launchers (one per source file).  They assume validated arguments.
+hipError_t launch_prefill_bf16(const moa_plan& p, const void* q, const void* k,
+                               const void* v, void* o, hipStream_t s);
+hipError_t launch_prefill_f32(const moa_plan& p, const void* q, const void* k,
+                              const void* v, void* o, hipStream_t s);
+hipError_t launch_kv_append(const moa_plan& p, void* kc, void* vc, const void* kn,
+                            const void* vn, int64_t pos0, int64_t n_new,
+                            hipStream_t s);
+hipError_t launch_decode_bf16(const moa_plan& p, const void* q, const void* kc,
+                              const void* vc, void* o, void* ws, hipStream_t s);
+
+// Workspace layout of the split-K decode: int32 tickets[B * Hkv] (padded to
+// 256 bytes; zero before first use, left zero by every call), then
+// float o[n_parts][G][D], then float2 ml[n_parts][G] (running max, sum),
+// n_parts = B * n_chunks.
+struct DecodeWs {
+  int* counters;
+  float* o;
+  float2* ml;
+};
+
+inline size_t decode_ws_counter_bytes(const moa_plan& p) {
+  return (((size_t)p.B * (size_t)p.Hkv * sizeof(int)) + 255) & ~(size_t)255;
+}
+
+inline size_t decode_ws_bytes(const moa_plan& p) {
+  const size_t parts = (size_t)p.B * (size_t)p.n_chunks;
+  size_t bytes = decode_ws_counter_bytes(p) + parts * (size_t)p.G * ((size_t)p.D + 2) * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+inline DecodeWs decode_ws_layout(const moa_plan& p, void* ws) {
+  const size_t parts = (size_t)p.B * (size_t)p.n_chunks;
+  char* base = static_cast<char*>(ws);
+  DecodeWs w;
+  w.counters = reinterpret_cast<int*>(base);
+  w.o = reinterpret_cast<float*>(base + decode_ws_counter_bytes(p));
+  w.ml = reinterpret_cast<float2*>(w.o + parts * (size_t)p.G * (size_t)p.D);
+  return w;
+}
+
+}  // namespace moa

@@ -1,0 +1,335 @@
+// Prefill attention with a per-head sliding window (gfx950).
+//
+// o[b,h,i] = sum over j in [max(0, i - S + 1), i] of softmax_j(q_i.k_j/sqrt(D)) v_j,
+// S the span of KV head h / G.  Blog digest "MoA: Mixture of Sparse Attention
+// for Automatic Large Language Model Compression", section 2.1: a
+// sliding-window mask is the base pattern; "Mixture of Attention" project
+// page, "Finding 2": each head has its own span, and the figure keeps a band
+// of the causal matrix.
+//
+// Work items come from the plan: 128 query rows of one (b, h_q) and the range
+// of 64-key tiles that hold at least one kept pair, longest items first.
+// Tiles outside the window are never loaded.
+//
+// bf16 kernel (4 waves, 32 query rows each):
+//  * S^T = K Q^T on 32x32x16 bf16 MFMA, so each lane owns one query row and
+//    the row max needs one exchange with the partner lane (l ^ 32);
+//  * key rows of a 32-key MFMA tile are permuted (row m = 16a + 8b + 4h + c
+//    reads key 16a + 8h + 4b + c), which puts the scores of lane half h on
+//    keys 16j + 8h .. +7 of P.V step j: the P^T operand is the lane's own
+//    scores, converted to bf16, with no data movement;
+//  * K tiles are staged in LDS row-major, V tiles transposed (V^T rows are
+//    the P.V A operand: 8 consecutive keys of one dimension per lane);
+//  * global loads of tile t+1 are in flight while tile t is computed;
+//  * masks are evaluated only on tiles a wave's rows do not fully keep, and a
+//    wave skips tiles none of its rows keep;
+//  * online softmax in fp32 with exp2 and the 1/sqrt(D)*log2(e) scale folded.
+//
+// f32 kernel (the float32 dtype): 2 threads per query row, each owning half
+// of the head dimension; K/V tiles in LDS; plain FMA arithmetic.
+
+#include "moa_device.h"
+#include "moa_internal.h"
+
+namespace moa {
+namespace {
+
+constexpr int BM = kPrefillBM;
+constexpr int BN = kPrefillBN;
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    bf16* __restrict__ o, const int4* __restrict__ items, const int32_t* __restrict__ span,
+    int Hq, int Hkv, int G, int N, float scale_log2) {
+  constexpr int KS = D / 16;       // k-steps of the Q.K product
+  constexpr int OT = D / 32;       // 32-dim tiles of the output
+  constexpr int KP = D + 8;        // K tile pitch (elements)
+  constexpr int VP = BN + 8;       // V^T tile pitch
+  constexpr int CPR = D / 8;       // 16-byte chunks per K row
+  constexpr int RPP = 256 / CPR;   // K rows per load pass
+  constexpr int KPASS = BN / RPP;
+  constexpr int NKG = 256 / CPR;   // V key groups
+  constexpr int KPT = BN / NKG;    // keys per thread in the V transpose
+  static_assert(KPT == 2 || KPT == 4, "V transpose");
+  __shared__ __attribute__((aligned(16))) bf16 Ks[BN * KP];
+  __shared__ __attribute__((aligned(16))) bf16 Vt[D * VP];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int half = lane >> 5;
+
+  const int4 it = items[blockIdx.x];
+  const int bh = it.x, qt = it.y, kt_lo = it.z, kt_hi = it.w;
+  const int b = bh / Hq;
+  const int hq = bh - b * Hq;
+  const int hkv = hq / G;
+  const int S = span[hkv];
+  const bf16* qb = q + (int64_t)bh * N * D;
+  const bf16* kb = k + ((int64_t)b * Hkv + hkv) * N * D;
+  const bf16* vb = v + ((int64_t)b * Hkv + hkv) * N * D;
+  bf16* ob = o + (int64_t)bh * N * D;
+
+  const int iw0 = qt * BM + wave * 32;  // first query row of this wave
+  const int my_q = iw0 + l32;
+
+  bf16x8 qop[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+    qop[s] = my_q < N ? ld16(qb + (int64_t)my_q * D + 16 * s + 8 * half) : zero_bf16x8();
+
+  floatx16 acc[OT];
+#pragma unroll
+  for (int t = 0; t < OT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // staging registers for one K/V tile
+  bf16x8 kst[KPASS];
+  bf16x8 vst[KPT];
+  const int kchunk = tid % CPR;
+  const int krow0 = tid / CPR;
+  const int vdg = tid / NKG;  // 8-dim group of the V transpose
+  const int vkg = tid % NKG;  // key group of the V transpose
+
+  auto load_tile = [&](int kt) {
+    const int j0 = kt * BN;
+#pragma unroll
+    for (int i = 0; i < KPASS; ++i) {
+      const int key = j0 + krow0 + i * RPP;
+      kst[i] = key < N ? ld16(kb + (int64_t)key * D + 8 * kchunk) : zero_bf16x8();
+    }
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int key = j0 + vkg * KPT + i;
+      vst[i] = key < N ? ld16(vb + (int64_t)key * D + 8 * vdg) : zero_bf16x8();
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < KPASS; ++i) st16(&Ks[(krow0 + i * RPP) * KP + 8 * kchunk], kst[i]);
+    u32x4 w[KPT];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) w[i] = __builtin_bit_cast(u32x4, vst[i]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      bf16* dst = &Vt[(8 * vdg + e) * VP + vkg * KPT];
+      if constexpr (KPT == 4) {
+        u32x2 pk;
+        pk[0] = __builtin_amdgcn_perm(w[1][e >> 1], w[0][e >> 1], sel);
+        pk[1] = __builtin_amdgcn_perm(w[3][e >> 1], w[2][e >> 1], sel);
+        *reinterpret_cast<u32x2*>(dst) = pk;
+      } else {
+        *reinterpret_cast<uint32_t*>(dst) = __builtin_amdgcn_perm(w[1][e >> 1], w[0][e >> 1], sel);
+      }
+    }
+  };
+
+  // key row of MFMA row l32 in each 32-key tile (see the file comment)
+  const int kperm = 16 * (l32 >> 4) + 8 * ((l32 >> 2) & 1) + 4 * ((l32 >> 3) & 1) + (l32 & 3);
+
+  load_tile(kt_lo);
+  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+    __syncthreads();
+    store_tile();
+    __syncthreads();
+    if (kt < kt_hi) load_tile(kt + 1);
+
+    const int j0 = kt * BN;
+    const bool active = iw0 < N && j0 <= iw0 + 31 && j0 + BN - 1 >= iw0 - S + 1;
+    if (!active) continue;
+    const bool full = j0 + BN - 1 <= iw0 && j0 >= iw0 + 31 - S + 1 && j0 + BN <= N;
+
+    floatx16 st[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st[t][r] = 0.f;
+      const bf16* krow = &Ks[(32 * t + kperm) * KP + 8 * half];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) st[t] = mfma32(ld16(krow + 16 * s), qop[s], st[t]);
+    }
+    // st[t][r] is the score of query my_q and key j0 + 32t + 16(r>>3) + 8half + (r&7)
+    if (!full) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = j0 + 32 * t + 16 * (r >> 3) + 8 * half + (r & 7);
+          const bool ok = key <= my_q && key >= my_q - S + 1 && key < N;
+          st[t][r] = ok ? st[t][r] : -INFINITY;
+        }
+    }
+    float mx = st[0][0];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[t][r]);
+    mx = wave_max_xor(mx, 32);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;  // row with no kept key yet
+    const float alpha = fast_exp2((m_run - m_use) * scale_log2);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int t = 0; t < OT; ++t) acc[t] *= alpha;
+    const float mb = m_use * scale_log2;
+    float p[2][16];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[t][r] = fast_exp2(__builtin_fmaf(st[t][r], scale_log2, -mb));
+        l_run += p[t][r];
+      }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8 pop = to_bf16x8(&p[j >> 1][8 * (j & 1)]);
+      const bf16* vrow = &Vt[l32 * VP + 16 * j + 8 * half];
+#pragma unroll
+      for (int t = 0; t < OT; ++t) acc[t] = mfma32(ld16(vrow + 32 * t * VP), pop, acc[t]);
+    }
+  }
+
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (my_q >= N) return;
+  const float inv = 1.f / l_run;
+  bf16* orow = ob + (int64_t)my_q * D;
+#pragma unroll
+  for (int t = 0; t < OT; ++t)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      bf16x4 x;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) x[c] = (bf16)(acc[t][4 * a + c] * inv);
+      *reinterpret_cast<bf16x4*>(orow + 32 * t + 8 * a + 4 * half) = x;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void prefill_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    float* __restrict__ o, const int4* __restrict__ items, const int32_t* __restrict__ span,
+    int Hq, int Hkv, int G, int N, float scale_log2) {
+  constexpr int DH = D / 2;
+  __shared__ __attribute__((aligned(16))) float Ks[BN * D];
+  __shared__ __attribute__((aligned(16))) float Vs[BN * D];
+  const int tid = threadIdx.x;
+  const int half = tid & 1;
+  const int4 it = items[blockIdx.x];
+  const int bh = it.x, qt = it.y, kt_lo = it.z, kt_hi = it.w;
+  const int b = bh / Hq;
+  const int hq = bh - b * Hq;
+  const int hkv = hq / G;
+  const int S = span[hkv];
+  const float* kb = k + ((int64_t)b * Hkv + hkv) * N * D;
+  const float* vb = v + ((int64_t)b * Hkv + hkv) * N * D;
+  const int my_q = qt * BM + (tid >> 1);
+
+  float qr[DH];
+  const float* qrow = q + ((int64_t)bh * N + (my_q < N ? my_q : 0)) * D + half * DH;
+#pragma unroll
+  for (int e = 0; e < DH; e += 4) {
+    const float4 x = *reinterpret_cast<const float4*>(qrow + e);
+    qr[e] = x.x; qr[e + 1] = x.y; qr[e + 2] = x.z; qr[e + 3] = x.w;
+  }
+  float acc[DH];
+#pragma unroll
+  for (int e = 0; e < DH; ++e) acc[e] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+    const int j0 = kt * BN;
+    __syncthreads();
+    for (int i = tid; i < BN * D / 4; i += 256) {
+      const int key = j0 + (i * 4) / D;
+      float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
+      if (key < N) {
+        kx = *reinterpret_cast<const float4*>(kb + (int64_t)j0 * D + 4 * i);
+        vx = *reinterpret_cast<const float4*>(vb + (int64_t)j0 * D + 4 * i);
+      }
+      *reinterpret_cast<float4*>(&Ks[4 * i]) = kx;
+      *reinterpret_cast<float4*>(&Vs[4 * i]) = vx;
+    }
+    __syncthreads();
+    float sc[BN];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < BN; ++j) {
+      const float* kr = &Ks[j * D + half * DH];
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < DH; ++e) s = __builtin_fmaf(qr[e], kr[e], s);
+      s += __shfl_xor(s, 1, 64);
+      const int key = j0 + j;
+      const bool ok = key <= my_q && key >= my_q - S + 1 && key < N;
+      sc[j] = ok ? s : -INFINITY;
+      mx = fmaxf(mx, sc[j]);
+    }
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2((m_run - m_use) * scale_log2);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int e = 0; e < DH; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int j = 0; j < BN; ++j) {
+      // (s - m) first: a score equal to the running max gives exactly 1
+      const float p = exp2f((sc[j] - m_use) * scale_log2);
+      l_run += p;
+      const float* vr = &Vs[j * D + half * DH];
+#pragma unroll
+      for (int e = 0; e < DH; ++e) acc[e] = __builtin_fmaf(p, vr[e], acc[e]);
+    }
+  }
+  if (my_q >= N) return;
+  const float inv = 1.f / l_run;
+  float* orow = o + ((int64_t)bh * N + my_q) * D + half * DH;
+#pragma unroll
+  for (int e = 0; e < DH; e += 4)
+    *reinterpret_cast<float4*>(orow + e) =
+        make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv);
+}
+
+}  // namespace
+
+hipError_t launch_prefill_bf16(const moa_plan& p, const void* q, const void* k, const void* v,
+                               void* o, hipStream_t s) {
+  const unsigned n_items = (unsigned)(p.prefill_items.size() / 4);
+  const float scale_log2 = kLog2e / sqrtf((float)p.D);
+  if (p.D == 64)
+    hipLaunchKernelGGL(prefill_bf16_kernel<64>, dim3(n_items), dim3(256), 0, s,
+                       static_cast<const bf16*>(q), static_cast<const bf16*>(k),
+                       static_cast<const bf16*>(v), static_cast<bf16*>(o), p.dev.prefill_items,
+                       p.dev.span, p.Hq, p.Hkv, p.G, (int)p.N, scale_log2);
+  else
+    hipLaunchKernelGGL(prefill_bf16_kernel<128>, dim3(n_items), dim3(256), 0, s,
+                       static_cast<const bf16*>(q), static_cast<const bf16*>(k),
+                       static_cast<const bf16*>(v), static_cast<bf16*>(o), p.dev.prefill_items,
+                       p.dev.span, p.Hq, p.Hkv, p.G, (int)p.N, scale_log2);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_f32(const moa_plan& p, const void* q, const void* k, const void* v,
+                              void* o, hipStream_t s) {
+  const unsigned n_items = (unsigned)(p.prefill_items.size() / 4);
+  const float scale_log2 = kLog2e / sqrtf((float)p.D);
+  if (p.D == 64)
+    hipLaunchKernelGGL(prefill_f32_kernel<64>, dim3(n_items), dim3(256), 0, s,
+                       static_cast<const float*>(q), static_cast<const float*>(k),
+                       static_cast<const float*>(v), static_cast<float*>(o), p.dev.prefill_items,
+                       p.dev.span, p.Hq, p.Hkv, p.G, (int)p.N, scale_log2);
+  else
+    hipLaunchKernelGGL(prefill_f32_kernel<128>, dim3(n_items), dim3(256), 0, s,
+                       static_cast<const float*>(q), static_cast<const float*>(k),
+                       static_cast<const float*>(v), static_cast<float*>(o), p.dev.prefill_items,
+                       p.dev.span, p.Hq, p.Hkv, p.G, (int)p.N, scale_log2);
+  return hipGetLastError();
+}
+
+}  // namespace moa

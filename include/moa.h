@@ -1,0 +1,202 @@
+/*
+ * moa.h -- C ABI of libmoa, heterogeneous sliding-window attention on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  Every KV head h has its own causal window of S_h keys:
+ * a query at position i attends keys max(0, i - S_h + 1) .. i.  The span
+ * follows the linear rule S = alpha + beta * N of the "Mixture of Attention"
+ * project page (section "Finding 2"), rounded up to the 64-wide compute block
+ * (section "Elastic search space" asks candidate spans to respect the
+ * hardware block size) and clamped to [1, N] (Finding 2's head B saturates at
+ * the input length).  Decode reads a fixed-size, head-specific KV cache of S_h
+ * slots per head (project page, "Demo" step 03 and "Inference speed and
+ * memory efficiency"; the blog digest "MoA: Mixture of Sparse Attention for
+ * Automatic Large Language Model Compression", section 5, describes the
+ * kernel's static KV cache).
+ *
+ * Conventions used by every entry point.
+ *  - B batch, Hq query heads, Hkv KV heads (Hq % Hkv == 0, G = Hq / Hkv),
+ *    D head dimension (64 or 128), N prompt length.  Query head h reads KV
+ *    head h / G.
+ *  - Element type: the plan's dtype (MOA_F32 = IEEE float32, MOA_BF16 =
+ *    bfloat16).  Accumulation is float32 for both.  Softmax scale 1/sqrt(D).
+ *  - Device pointers are hipMalloc'ed (or torch CUDA/HIP) memory on the
+ *    current device, owned by the caller, contiguous, 16-byte aligned.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *    device work is enqueued asynchronously on it; no call synchronises.
+ *  - Return value: MOA_OK (0) or a negative moa_status.  On failure no device
+ *    work has been enqueued and moa_last_error() describes the problem (a
+ *    thread-local string, valid until the next failing call on the thread).
+ *    Faults inside kernels surface at the caller's next synchronisation, as
+ *    with any HIP launch.
+ *  - Threads: a plan is read-only after creation; distinct threads and
+ *    streams may use one plan concurrently.  Calls that write the same cache
+ *    or workspace must be ordered by the caller.
+ *
+ * KV cache ("ring pool") layout.  One pool for K and one for V, each of
+ * B * slots_per_seq * D elements, slots_per_seq = sum_h S_h.  Head h of
+ * sequence b owns slots offset[h] .. offset[h] + S_h - 1, offset being the
+ * exclusive prefix sum of the spans.  Absolute position p of head h lives in
+ * slot p mod S_h.
+ *    K element (b, h, slot, d) at  (b*slots_per_seq + offset[h] + slot)*D + d
+ *    V element (b, h, slot, d) at  (b*slots_per_seq + offset[h])*D + d*S_h + slot
+ * (V rings are stored dimension-major so that decode's P.V product reads
+ * consecutive slots of one dimension as a matrix-core operand.)
+ */
+#ifndef MOA_H
+#define MOA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOA_OK = 0,
+  MOA_EINVAL = -1,        /* bad argument: null pointer, bad size, bad rule */
+  MOA_EUNSUPPORTED = -2,  /* valid but not implemented (e.g. head_dim 96)  */
+  MOA_ENOMEM = -3,        /* host or device allocation of plan tables failed */
+  MOA_EHIP = -4,          /* a HIP runtime call failed (message has the code) */
+  MOA_EWORKSPACE = -5     /* decode workspace smaller than required          */
+} moa_status;
+
+typedef enum { MOA_F32 = 0, MOA_BF16 = 1 } moa_dtype;
+
+/* The problem a plan is built for: shapes plus one (alpha, beta) rule per KV
+ * head (project page, "Finding 2").  alpha and beta are host arrays of
+ * n_kv_heads entries, read during moa_plan_create only.  alpha >= 0 and beta
+ * >= 0 finite are required. */
+typedef struct {
+  int32_t batch;        /* B >= 1 */
+  int32_t n_q_heads;    /* Hq >= 1 */
+  int32_t n_kv_heads;   /* Hkv >= 1, divides Hq, G = Hq/Hkv <= 16 */
+  int32_t head_dim;     /* D: 64 or 128 */
+  int64_t n_prompt;     /* N >= 1, < 2^31 */
+  const int64_t* alpha; /* [n_kv_heads] */
+  const double* beta;   /* [n_kv_heads] */
+  int32_t dtype;        /* moa_dtype */
+} moa_problem;
+
+typedef struct moa_plan* moa_plan_t;
+
+/* moa_plan_create flags */
+#define MOA_PLAN_HOST_ONLY 1u  /* build host tables only: no device memory is
+                                  touched, compute entry points then fail with
+                                  MOA_EINVAL.  For inspecting tables on a
+                                  machine without a GPU. */
+
+/* ---- host-only table builders (no GPU needed) ---------------------------- */
+
+/* Span table.  span[h] = clamp(64 * ceil(x / 64), 1, N) with
+ * x = (double)alpha[h] + beta[h] * (double)N evaluated in IEEE double with one
+ * rounding per operation (no fused multiply-add); x >= N gives N.  Project
+ * page, "Finding 2" (linear rule, saturation at N) and "Elastic search space"
+ * (block-size alignment).  span: host array of n_kv_heads int32, written by
+ * the call.  Errors: MOA_EINVAL for null arrays, n_kv_heads < 1, N < 1 or
+ * N >= 2^31, alpha < 0, beta < 0 or beta not finite. */
+int moa_spans(const int64_t* alpha, const double* beta, int32_t n_kv_heads,
+              int64_t n_prompt, int32_t* span);
+
+/* Ring offsets: offset[h] = sum of span[0..h-1] (host int64 array of
+ * n_kv_heads), *slots_per_seq = sum of all spans.  Project page, "Demo" step
+ * 03: a fixed-size cache per head.  Errors: MOA_EINVAL for null pointers,
+ * n_kv_heads < 1 or any span < 1. */
+int moa_ring_offsets(const int32_t* span, int32_t n_kv_heads, int64_t* offset,
+                     int64_t* slots_per_seq);
+
+/* ---- plans ---------------------------------------------------------------- */
+
+/* Validate `problem`, build the span, offset and work tables, and (unless
+ * MOA_PLAN_HOST_ONLY) copy them to the current HIP device.  *out receives a
+ * plan owned by the caller, released with moa_plan_destroy.  Errors:
+ * MOA_EINVAL (bad shapes or rules), MOA_EUNSUPPORTED (head_dim not 64/128,
+ * G > 16, unknown dtype), MOA_ENOMEM, MOA_EHIP. */
+int moa_plan_create(const moa_problem* problem, uint32_t flags, moa_plan_t* out);
+
+/* Free the plan's host and device tables.  NULL is accepted.  The caller must
+ * ensure no enqueued work still reads the plan (synchronise first). */
+int moa_plan_destroy(moa_plan_t plan);
+
+/* Host copies of the plan's tables; any output pointer may be NULL.
+ * span: int32[n_kv_heads]; offset: int64[n_kv_heads]. */
+int moa_plan_tables(moa_plan_t plan, int32_t* span, int64_t* offset,
+                    int64_t* slots_per_seq);
+
+/* Elements in ONE cache pool (K or V): B * slots_per_seq * D.  0 on error. */
+int64_t moa_cache_elems(moa_plan_t plan);
+
+/* Bytes of device workspace moa_decode needs (>= 256).  0 on error.  The
+ * workspace must be zero-filled before its first moa_decode call; every
+ * completed call leaves it ready for the next (its tickets back at zero). */
+size_t moa_decode_workspace_bytes(moa_plan_t plan);
+
+/* Work-list inspection, for tests.  Prefill items are int32 quadruples
+ * {b * Hq + h_q, q_tile, kt_lo, kt_hi}: query rows q_tile*128 .. +127 read
+ * key tiles kt_lo .. kt_hi (64 keys each), i.e. every tile holding at least
+ * one kept (query, key) pair and no other.  Items are in launch order: cost
+ * (kt_hi - kt_lo + 1) descending, ties by (b*Hq + h_q, q_tile) ascending.
+ * Decode chunks are int32 triples {h_kv, first_slot, n_slots} for one
+ * sequence, in launch order; each head's ring is cut into chunks of at most
+ * moa_plan_decode_chunk() slots.  Pass out = NULL to get the count; the
+ * return value is the item count (>= 0) or a negative moa_status. */
+int64_t moa_plan_prefill_items(moa_plan_t plan, int32_t* out);
+int64_t moa_plan_decode_chunks(moa_plan_t plan, int32_t* out);
+int32_t moa_plan_decode_chunk(moa_plan_t plan);
+
+/* ---- the hot path --------------------------------------------------------- */
+
+/* Prefill attention, every head at once.
+ *   q [B, Hq, N, D], k and v [B, Hkv, N, D] (inputs), o [B, Hq, N, D]
+ *   (output), all in the plan's dtype.
+ *   o[b,h,i,:] = sum_{j=max(0,i-S+1)}^{i} softmax_j(q_i . k_j / sqrt(D)) v_j,
+ *   S = span of KV head h / G.
+ * Blog digest section 2.1 (sliding-window base mask) and project page
+ * "Finding 2" (per-head span; the figure keeps a band of the causal matrix).
+ * Key tiles outside a head's window are never read.  Errors: MOA_EINVAL for
+ * null pointers or a host-only plan; MOA_EHIP if the launch fails. */
+int moa_prefill(moa_plan_t plan, const void* q, const void* k, const void* v,
+                void* o, void* stream);
+
+/* Write positions pos0 .. pos0 + n_new - 1 of every (b, h) into the ring
+ * pools.  k_new, v_new: [B, Hkv, n_new, D] in the plan's dtype; row t holds
+ * position pos0 + t.  Only the last S_h of them are written for head h (the
+ * earlier ones would be overwritten in the same call), each into slot
+ * p mod S_h.  pos0 = 0, n_new = N hands a prompt's K/V over to the cache
+ * after prefill; n_new = 1, pos0 = p appends one decode token.  Errors:
+ * MOA_EINVAL for null pointers, pos0 < 0, n_new < 1 or a host-only plan. */
+int moa_kv_append(moa_plan_t plan, void* k_cache, void* v_cache,
+                  const void* k_new, const void* v_new, int64_t pos0,
+                  int64_t n_new, void* stream);
+
+/* Decode attention for the token at absolute position pos >= N, whose key
+ * and value moa_kv_append must already have written (append, then attend).
+ * The span stays the one computed from the prompt length N (the deployed
+ * cache has a fixed size), so head h attends positions pos - S_h + 1 .. pos,
+ * which are exactly the S_h slots of its ring.
+ *   q [B, Hq, D] (input), o [B, Hq, D] (output), plan dtype MOA_BF16.
+ * Split-K, one kernel launch: each head's ring is cut into chunks of at
+ * most moa_plan_decode_chunk() slots; a head with one chunk writes o
+ * directly, otherwise each chunk writes its partial (max, sum, P.V) to
+ * `workspace` and takes a ticket, and the last chunk of the (sequence, KV
+ * head) merges the partials in chunk order.  workspace: device memory of at
+ * least moa_decode_workspace_bytes bytes, zero-filled before its first use
+ * (any plan may reuse it afterwards; calls that overlap on one workspace
+ * race).  Errors: MOA_EINVAL (null pointers, pos < N, host-only plan),
+ * MOA_EUNSUPPORTED (dtype MOA_F32), MOA_EWORKSPACE. */
+int moa_decode(moa_plan_t plan, const void* q, const void* k_cache,
+               const void* v_cache, int64_t pos, void* o, void* workspace,
+               size_t ws_bytes, void* stream);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* moa_last_error(void);
+
+/* Library version string. */
+const char* moa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOA_H */

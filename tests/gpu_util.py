@@ -1,0 +1,53 @@
+"""Helpers shared by the GPU parity tests (test code, not product code)."""
+
+import sys
+
+import numpy as np
+import torch
+
+
+def log(msg):
+    """Name the case before each GPU step, so a failing run says which it was."""
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def f64(t):
+    """Torch tensor (any device / float dtype) -> float64 numpy array."""
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def ring_k(pool, plan, b, h):
+    """[S_h, D] view of K ring (b, h) in the layout include/moa.h documents."""
+    s, d = int(plan.spans[h]), plan.head_dim
+    base = (b * plan.slots_per_seq + int(plan.offsets[h])) * d
+    return pool[base:base + s * d].view(s, d)
+
+
+def ring_v(pool, plan, b, h):
+    """[S_h, D] view of V ring (b, h): stored dimension-major, returned slot-major."""
+    s, d = int(plan.spans[h]), plan.head_dim
+    base = (b * plan.slots_per_seq + int(plan.offsets[h])) * d
+    return pool[base:base + s * d].view(d, s).t()
+
+
+def ring_positions(s, p_last):
+    """Absolute position held by each slot of a ring of s slots after p_last (slot = p mod s)."""
+    pos = np.empty(s, dtype=np.int64)
+    for p in range(p_last - s + 1, p_last + 1):
+        pos[p % s] = p
+    return pos
+
+
+def sample_rows(n, s, count, seed):
+    """Edge rows of a head with span s plus seeded random rows, sorted and unique."""
+    edges = [0, 1, 63, 64, 127, 128, s - 2, s - 1, s, s + 1, n - 129, n - 128, n - 65, n - 64,
+             n - 2, n - 1]
+    rng = np.random.Generator(np.random.PCG64(seed))
+    rows = set(r for r in edges if 0 <= r < n)
+    rows.update(int(x) for x in rng.integers(0, n, count))
+    return sorted(rows)
+
+
+def max_err(got, want):
+    return float(np.max(np.abs(np.asarray(got, dtype=np.float64) - want))) if np.size(want) else 0.0

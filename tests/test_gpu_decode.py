@@ -1,0 +1,185 @@
+"""Ring append and split-K decode parity: HIP kernels against the oracle.
+
+Ring contents are compared bit for bit (bf16 bits) with the oracle's
+expected slot contents read through the layout include/moa.h documents;
+decode outputs within max-abs 2e-2 of the float64 oracle on the same bits.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import f64, log, max_err, ring_k, ring_positions, ring_v
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def _prompt_and_steps(bsz, hq, hkv, n, d, t_steps, seed):
+    _, kp, vp = workloads.prefill_inputs(bsz, hq, hkv, n, d, "bf16", seed)
+    qs, ks, vs = workloads.decode_step_inputs(bsz, hq, hkv, t_steps, d, "bf16", seed + 1)
+    return kp, vp, qs, ks, vs
+
+
+def _check_rings(plan, kc, vc, kp, vp, ks, vs, n, t_done):
+    """Every slot of every ring holds the bits of the position it should."""
+    p_last = n - 1 + t_done
+    kc_h, vc_h = kc.cpu(), vc.cpu()
+    for b in range(plan.batch):
+        for h in range(plan.n_kv_heads):
+            s = int(plan.spans[h])
+            hist_k = torch.cat([kp[b, h], ks[:t_done, b, h]]) if t_done else kp[b, h]
+            hist_v = torch.cat([vp[b, h], vs[:t_done, b, h]]) if t_done else vp[b, h]
+            pos = np.arange(n + t_done)
+            exp_k, held = oracle.ring_expected(hist_k.view(torch.int16).numpy(), pos, s, p_last)
+            exp_v, _ = oracle.ring_expected(hist_v.view(torch.int16).numpy(), pos, s, p_last)
+            assert (held == ring_positions(s, p_last)).all()
+            assert np.array_equal(ring_k(kc_h, plan, b, h).view(torch.int16).numpy(), exp_k), (b, h)
+            assert np.array_equal(ring_v(vc_h, plan, b, h).contiguous().view(torch.int16).numpy(),
+                                  exp_v), (b, h)
+
+
+CASES = [
+    # B, Hq, Hkv, D, N, alpha, beta, T
+    (3, 4, 2, 128, 300, [0, 100], [0.0, 0.0], 5),
+    (2, 4, 4, 128, 300, [0, 64, 0, 0], [0.0, 0.0, 1.0, 0.5], 4),
+    (2, 16, 2, 128, 2500, [0, 1500], [1.0, 0.0], 4),
+    (2, 8, 1, 64, 1100, [0], [0.97], 3),
+    (1, 1, 1, 128, 5, [0], [0.5], 6),
+    (2, 6, 3, 64, 2049, [0, 64, 2000], [1.0, 0.0, 0.0], 3),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_handoff_append_decode(moa, case):
+    bsz, hq, hkv, d, n, alpha, beta, t_steps = CASES[case]
+    log(f"decode case {case}: B{bsz} Hq{hq} Hkv{hkv} D{d} N{n} T{t_steps}")
+    plan = moa.Plan(bsz, hq, hkv, d, n, alpha, beta)
+    kp, vp, qs, ks, vs = _prompt_and_steps(bsz, hq, hkv, n, d, t_steps, 5000 + 10 * case)
+    kc, vc = plan.new_cache()
+    ws = plan.new_workspace()
+    plan.kv_append(kc, vc, kp.cuda(), vp.cuda(), 0)
+    torch.cuda.synchronize()
+    _check_rings(plan, kc, vc, kp, vp, ks, vs, n, 0)
+    outs = []
+    for t in range(t_steps):
+        plan.kv_append(kc, vc, ks[t].unsqueeze(2).cuda(), vs[t].unsqueeze(2).cuda(), n + t)
+        o = torch.empty(bsz, hq, d, dtype=torch.bfloat16, device="cuda")
+        plan.decode(qs[t].cuda(), kc, vc, n + t, o, ws)
+        outs.append(o)
+    torch.cuda.synchronize()
+    _check_rings(plan, kc, vc, kp, vp, ks, vs, n, t_steps)
+    want = oracle.decode(f64(qs), [f64(kp[:, h]) for h in range(hkv)],
+                         [f64(vp[:, h]) for h in range(hkv)], f64(ks), f64(vs), plan.spans, n)
+    got = np.stack([f64(o) for o in outs])
+    err = max_err(got, want)
+    log(f"case {case} spans {list(plan.spans)} max abs err {err:.3e}")
+    assert np.isfinite(got).all()
+    assert err <= TOL
+
+
+def test_decode_span_one_returns_new_value_exactly(moa):
+    log("decode span-1")
+    bsz, hq, hkv, d, n = 2, 4, 2, 128, 70
+    plan = moa.Plan(bsz, hq, hkv, d, n, [0, 0], [0.0, 0.0])
+    kp, vp, qs, ks, vs = _prompt_and_steps(bsz, hq, hkv, n, d, 2, 61)
+    kc, vc = plan.new_cache()
+    ws = plan.new_workspace()
+    plan.kv_append(kc, vc, kp.cuda(), vp.cuda(), 0)
+    for t in range(2):
+        plan.kv_append(kc, vc, ks[t].unsqueeze(2).cuda(), vs[t].unsqueeze(2).cuda(), n + t)
+        o = torch.empty(bsz, hq, d, dtype=torch.bfloat16, device="cuda")
+        plan.decode(qs[t].cuda(), kc, vc, n + t, o, ws)
+        assert torch.equal(o.cpu(), vs[t].repeat_interleave(2, dim=1))
+
+
+def test_decode_repeat_is_deterministic(moa):
+    """Same inputs twice give the same bits (no ordering-dependent reduction)."""
+    log("decode determinism")
+    bsz, hq, hkv, d, n = 2, 8, 2, 128, 3000
+    plan = moa.Plan(bsz, hq, hkv, d, n, [0, 0], [1.0, 0.6])
+    kp, vp, qs, ks, vs = _prompt_and_steps(bsz, hq, hkv, n, d, 1, 63)
+    kc, vc = plan.new_cache()
+    ws = plan.new_workspace()
+    plan.kv_append(kc, vc, kp.cuda(), vp.cuda(), 0)
+    plan.kv_append(kc, vc, ks[0].unsqueeze(2).cuda(), vs[0].unsqueeze(2).cuda(), n)
+    o1 = torch.empty(bsz, hq, d, dtype=torch.bfloat16, device="cuda")
+    o2 = torch.empty_like(o1)
+    plan.decode(qs[0].cuda(), kc, vc, n, o1, ws)
+    plan.decode(qs[0].cuda(), kc, vc, n, o2, ws)
+    assert torch.equal(o1, o2)
+
+
+def test_decode_argument_errors(moa):
+    log("decode argument errors")
+    plan = moa.Plan(1, 2, 2, 128, 64, [0, 0], [1.0, 1.0])
+    kc, vc = plan.new_cache()
+    q = torch.zeros(1, 2, 128, dtype=torch.bfloat16, device="cuda")
+    o = torch.empty_like(q)
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(moa.MoaError) as e:
+        plan.decode(q, kc, vc, 64, o, small)
+    assert e.value.status == moa.MOA_EWORKSPACE
+    with pytest.raises(moa.MoaError) as e:
+        plan.decode(q, kc, vc, 63, o, plan.new_workspace())
+    assert e.value.status == moa.MOA_EINVAL
+    f32 = moa.Plan(1, 2, 2, 128, 64, [0, 0], [1.0, 1.0], dtype="f32")
+    kf, vf = f32.new_cache()
+    with pytest.raises(moa.MoaError) as e:
+        f32.decode(q.float(), kf, vf, 64, o.float(), f32.new_workspace())
+    assert e.value.status == moa.MOA_EUNSUPPORTED
+    with pytest.raises(ValueError):
+        plan.decode(q[:, :1], kc, vc, 64, o, plan.new_workspace())
+
+
+@pytest.mark.parametrize("name", ["c2_decode", "c3_decode", "c4_decode"])
+def test_decode_full_size_sampled_heads(moa, name):
+    """Full-size rings (device-filled with seeded N(0,1)), a few steps, sampled (b, h) checked."""
+    w = workloads.WORKLOADS[name]
+    alpha, beta = workloads.rules(name)
+    plan = moa.Plan(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, alpha, beta)
+    log(f"{name}: filling {2 * plan.cache_elems * 2 / 1e9:.2f} GB of rings")
+    kc = workloads.device_normal_(torch.empty(plan.cache_elems, dtype=torch.bfloat16,
+                                              device="cuda"), 81)
+    vc = workloads.device_normal_(torch.empty(plan.cache_elems, dtype=torch.bfloat16,
+                                              device="cuda"), 82)
+    ws = plan.new_workspace()
+    t_steps = 3
+    n = w.n_prompt
+    g = w.n_q_heads // w.n_kv_heads
+    qs, ks, vs = workloads.decode_step_inputs(w.batch, w.n_q_heads, w.n_kv_heads, t_steps,
+                                              w.head_dim, "bf16", w.data_seed)
+    rng = np.random.Generator(np.random.PCG64(w.data_seed))
+    pairs = [(0, h) for h in range(w.n_kv_heads)] + [(w.batch - 1, h) for h in range(w.n_kv_heads)]
+    pairs += [(int(rng.integers(w.batch)), int(rng.integers(w.n_kv_heads))) for _ in range(8)]
+    # the prompt tail each sampled ring holds, ordered by position
+    init = {}
+    for b, h in pairs:
+        s = int(plan.spans[h])
+        order = np.argsort(ring_positions(s, n - 1))
+        init[(b, h)] = (f64(ring_k(kc, plan, b, h))[order], f64(ring_v(vc, plan, b, h))[order])
+    outs = []
+    for t in range(t_steps):
+        log(f"{name}: step {t}")
+        plan.kv_append(kc, vc, ks[t].unsqueeze(2).cuda(), vs[t].unsqueeze(2).cuda(), n + t)
+        o = torch.empty(w.batch, w.n_q_heads, w.head_dim, dtype=torch.bfloat16, device="cuda")
+        plan.decode(qs[t].cuda(), kc, vc, n + t, o, ws)
+        outs.append(o.cpu())
+    torch.cuda.synchronize()
+    worst = 0.0
+    for b, h in pairs:
+        s = int(plan.spans[h])
+        k0, v0 = init[(b, h)]
+        for t in range(t_steps):
+            hist_k = np.concatenate([k0, f64(ks[:t + 1, b, h])])
+            hist_v = np.concatenate([v0, f64(vs[:t + 1, b, h])])
+            pos = np.arange(n - s, n + t + 1)
+            want = oracle.decode_step(f64(qs[t, b, h * g:(h + 1) * g]), hist_k, hist_v, pos,
+                                      n + t, s)
+            err = max_err(f64(outs[t][b, h * g:(h + 1) * g]), want)
+            worst = max(worst, err)
+            assert err <= TOL, (name, b, h, s, t, err)
+    log(f"{name}: worst sampled err {worst:.3e}")

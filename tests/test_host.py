@@ -1,0 +1,236 @@
+"""Host-side tests of libmoa through its C ABI (no GPU needed).
+
+The library must load and export every symbol include/moa.h declares; its
+span and offset tables must equal the oracle's bit for bit; its work lists
+must match a brute force over the oracle's explicit mask; invalid arguments
+must be rejected with the documented status before any device work.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_exports_every_declared_symbol(moa):
+    with open(os.path.join(ROOT, "include", "moa.h")) as f:
+        header = f.read()
+    declared = sorted(set(re.findall(r"\b(moa_[a-z_]+)\s*\(", header)))
+    assert declared, "no declarations found"
+    assert sorted(moa.EXPORTS) == declared
+    lib = ctypes.CDLL(moa.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert "gfx950" in moa.version()
+
+
+def _rule_cases():
+    rng = np.random.Generator(np.random.PCG64(5))
+    cases = []
+    for n in (1, 2, 63, 64, 65, 100, 512, 777, 1000, 8192, 16384, 32768, 65536, 2**31 - 1):
+        alpha = [0, 1, 63, 64, 65, 512, 1600, 4096, 5600, 10**9] + list(rng.integers(0, 70000, 6))
+        beta = [0.0, 0.25, 0.5, 0.75, 1.0, 0.9, 1e-3, 0.3, 2.0, 0.1] + list(rng.random(6))
+        cases.append((alpha, beta, n))
+    return cases
+
+
+@pytest.mark.parametrize("case", range(14))
+def test_spans_bit_exact(moa, case):
+    alpha, beta, n = _rule_cases()[case]
+    assert list(moa.spans(alpha, beta, n)) == list(oracle.spans(alpha, beta, n))
+
+
+def test_spans_random_doubles(moa):
+    rng = np.random.Generator(np.random.PCG64(11))
+    for n in (100, 4097, 8192, 65536, 1_000_003):
+        alpha = rng.integers(0, 2 * n, 500)
+        beta = rng.random(500) * 1.5
+        assert list(moa.spans(alpha, beta, n)) == list(oracle.spans(alpha, beta, n))
+
+
+def test_ring_offsets_bit_exact(moa):
+    span = np.array([1, 64, 7, 8192, 3, 65536], dtype=np.int32)
+    off, tot = moa.ring_offsets(span)
+    o_off, o_tot = oracle.ring_offsets(span)
+    assert list(off) == list(o_off) and tot == o_tot
+
+
+@pytest.mark.parametrize("name", sorted(workloads.WORKLOADS))
+def test_workload_plan_tables(moa, name):
+    w = workloads.WORKLOADS[name]
+    alpha, beta = workloads.rules(name)
+    plan = moa.Plan(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, alpha, beta,
+                    dtype=w.dtype, host_only=True)
+    s = oracle.spans(alpha, beta, w.n_prompt)
+    assert list(plan.spans) == list(s)
+    off, tot = oracle.ring_offsets(s)
+    assert list(plan.offsets) == list(off) and plan.slots_per_seq == tot
+    assert plan.cache_elems == w.batch * tot * w.head_dim
+    if name == "c0_prefill":
+        assert list(plan.spans) == [64, 128, 256, 512]
+    plan.close()
+
+
+def _check_prefill_items(plan, n, span_of_q):
+    """Each (bh, q_tile) once; [kt_lo, kt_hi] = exactly the live 64-key tiles; LPT order."""
+    items = plan.prefill_items()
+    bhq = plan.batch * plan.n_q_heads
+    n_qt = (n + 127) // 128
+    assert len(items) == bhq * n_qt
+    seen = set()
+    for bh, qt, lo, hi in items:
+        assert (bh, qt) not in seen
+        seen.add((bh, qt))
+        s = span_of_q(bh % plan.n_q_heads)
+        rows = np.arange(qt * 128, min(qt * 128 + 128, n))
+        # brute force: live tiles from the explicit mask rows
+        m = oracle.band_mask(s, n)[rows]
+        live = [kt for kt in range((n + 63) // 64) if m[:, kt * 64:(kt + 1) * 64].any()]
+        assert live == list(range(lo, hi + 1)), (bh, qt, lo, hi, live[:3], live[-3:])
+    cost = items[:, 3] - items[:, 2]
+    assert (np.diff(cost) <= 0).all()
+    for i in range(1, len(items)):
+        if cost[i] == cost[i - 1]:
+            assert (items[i, 0], items[i, 1]) > (items[i - 1, 0], items[i - 1, 1])
+    return items
+
+
+@pytest.mark.parametrize("n,alpha,beta,hq,hkv", [
+    (1, [0], [0.0], 1, 1),
+    (200, [0, 64, 100, 0], [0.0, 0.0, 0.0, 1.0], 8, 4),
+    (1000, [0, 1, 512, 5000], [0.0, 0.1, 0.25, 0.0], 4, 4),
+    (777, [64, 0], [0.0, 0.5], 16, 2),
+])
+def test_prefill_items_bruteforce(moa, n, alpha, beta, hq, hkv):
+    plan = moa.Plan(2, hq, hkv, 128, n, alpha, beta, host_only=True)
+    s = oracle.spans(alpha, beta, n)
+    g = hq // hkv
+    _check_prefill_items(plan, n, lambda h: int(s[h // g]))
+
+
+def test_prefill_items_full_size_tables(moa):
+    """Tile ranges at the full prefill sizes, via the union-of-windows rule checked against mask rows."""
+    for name in ("c1_prefill", "c4_prefill"):
+        w = workloads.WORKLOADS[name]
+        alpha, beta = workloads.rules(name)
+        plan = moa.Plan(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, alpha, beta,
+                        host_only=True)
+        s = oracle.spans(alpha, beta, w.n_prompt)
+        items = plan.prefill_items()
+        g = w.n_q_heads // w.n_kv_heads
+        n = w.n_prompt
+        j = np.arange(n)
+        rng = np.random.Generator(np.random.PCG64(3))
+        for idx in rng.integers(0, len(items), 200):
+            bh, qt, lo, hi = items[idx]
+            sp = int(s[(bh % w.n_q_heads) // g])
+            r0, r1 = qt * 128, min(qt * 128 + 128, n) - 1
+            kept = np.zeros(n, dtype=bool)
+            for i in (r0, r1):                   # the band's extreme rows bound the union
+                kept |= (j <= i) & (j >= i - sp + 1)
+            kept[max(0, r0 - sp + 1):r1 + 1] = True
+            tiles = np.nonzero(kept.reshape(-1, 64).any(axis=1))[0]
+            assert (tiles.min(), tiles.max()) == (lo, hi)
+        plan.close()
+
+
+@pytest.mark.parametrize("name", ["c2_decode", "c3_decode", "c4_decode"])
+def test_decode_chunks_cover_rings(moa, name):
+    w = workloads.WORKLOADS[name]
+    alpha, beta = workloads.rules(name)
+    plan = moa.Plan(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, alpha, beta,
+                    host_only=True)
+    ch = plan.decode_chunks()
+    c = plan.decode_chunk
+    for h, s in enumerate(plan.spans):
+        mine = ch[ch[:, 0] == h]
+        assert len(mine) == -(-int(s) // c)
+        covered = np.zeros(int(s), dtype=int)
+        for _, first, cnt in mine:
+            assert 1 <= cnt <= c
+            covered[first:first + cnt] += 1
+        assert (covered == 1).all()
+    assert plan.workspace_bytes >= w.batch * len(ch) * (w.n_q_heads // w.n_kv_heads) * \
+        (w.head_dim + 2) * 4
+    plan.close()
+
+
+# ---------------------------------------------------------------------------
+# error paths (checked before any device work, so they run without a GPU)
+# ---------------------------------------------------------------------------
+
+def _plan_err(moa, **kw):
+    args = dict(batch=1, n_q_heads=4, n_kv_heads=2, head_dim=128, n_prompt=100,
+                alpha=[0, 0], beta=[0.5, 0.5], dtype="bf16", host_only=True)
+    args.update(kw)
+    with pytest.raises(moa.MoaError) as e:
+        moa.Plan(**args)
+    return e.value.status
+
+
+def test_plan_errors(moa):
+    assert _plan_err(moa, n_q_heads=3) == moa.MOA_EINVAL
+    assert _plan_err(moa, head_dim=96) == moa.MOA_EUNSUPPORTED
+    assert _plan_err(moa, n_q_heads=64, n_kv_heads=2) == moa.MOA_EUNSUPPORTED
+    assert _plan_err(moa, alpha=[-1, 0]) == moa.MOA_EINVAL
+    assert _plan_err(moa, beta=[float("nan"), 0.0]) == moa.MOA_EINVAL
+    assert _plan_err(moa, beta=[float("inf"), 0.0]) == moa.MOA_EINVAL
+    assert _plan_err(moa, beta=[-0.5, 0.0]) == moa.MOA_EINVAL
+    assert _plan_err(moa, batch=0) == moa.MOA_EINVAL
+    assert _plan_err(moa, n_prompt=0) == moa.MOA_EINVAL
+    assert _plan_err(moa, n_prompt=2**31) == moa.MOA_EINVAL
+    assert "multiple" in moa.last_error() or "n_prompt" in moa.last_error()
+
+
+def test_raw_abi_errors(moa):
+    lib = moa._lib
+    out = moa._P()
+    assert lib.moa_plan_create(None, 0, ctypes.byref(out)) == moa.MOA_EINVAL
+    assert "NULL" in moa.last_error()
+    assert lib.moa_plan_create(None, 0, None) == moa.MOA_EINVAL
+    assert lib.moa_spans(None, None, 1, 10, None) == moa.MOA_EINVAL
+    assert lib.moa_plan_destroy(None) == moa.MOA_OK
+    assert lib.moa_prefill(None, None, None, None, None, None) == moa.MOA_EINVAL
+    assert lib.moa_cache_elems(None) == 0
+    assert lib.moa_decode_workspace_bytes(None) == 0
+    # unknown flag bits
+    a, ap = moa._i64([0])
+    b, bp = moa._f64([1.0])
+    pr = moa._Problem(1, 1, 1, 128, 10, ap, bp, moa.MOA_BF16)
+    assert lib.moa_plan_create(ctypes.byref(pr), 0x10, ctypes.byref(out)) == moa.MOA_EINVAL
+    pr.dtype = 7
+    assert lib.moa_plan_create(ctypes.byref(pr), moa.MOA_PLAN_HOST_ONLY,
+                               ctypes.byref(out)) == moa.MOA_EUNSUPPORTED
+
+
+def test_host_only_plan_refuses_compute(moa):
+    plan = moa.Plan(1, 2, 2, 64, 50, [0, 0], [1.0, 1.0], host_only=True)
+    lib = moa._lib
+    dummy = ctypes.c_void_p(16)   # never dereferenced: the plan check fails first
+    assert lib.moa_prefill(plan._h, dummy, dummy, dummy, dummy, None) == moa.MOA_EINVAL
+    assert "HOST_ONLY" in moa.last_error()
+    assert lib.moa_kv_append(plan._h, dummy, dummy, dummy, dummy, 0, 1, None) == moa.MOA_EINVAL
+    assert lib.moa_decode(plan._h, dummy, dummy, dummy, 50, dummy, dummy, 1 << 30,
+                          None) == moa.MOA_EINVAL
+    plan.close()
+
+
+def test_error_message_is_thread_local(moa):
+    import threading
+    moa._lib.moa_spans(None, None, 1, 10, None)
+    msgs = []
+
+    def other():
+        msgs.append(moa.last_error())
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert msgs == [""]
+    assert moa.last_error() != ""
