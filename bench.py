@@ -5,7 +5,8 @@
 
 A step is one decode step of the whole batch: the new token's K/V appended
 to every head's ring (moa_kv_append, n_new = 1), then split-K decode
-attention over the rings (moa_decode, one kernel).  The default workload is
+attention over the rings (moa_decode: a split-K partial kernel and a small
+combine kernel).  The default workload is
 the Vicuna-7B-shaped decode (B64, H32, D128, prompt 16384, 50 % mean
 density); `value` is decode tokens/s of that batch (B tokens per step) with
 every input resident in HBM.  The same run times the Vicuna-7B-shaped
@@ -255,6 +256,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes 5 times (the "
+                         "known-size kernel that scales the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the attention path has "
@@ -262,10 +266,19 @@ def main():
         sys.exit(2)
 
     import torch
-    import heterogeneous_sliding_windows_amd as moa
-    import workloads
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 5}))
+        return
+    import heterogeneous_sliding_windows_amd as moa
+    import workloads
 
     log(f"decode workload {args.workload}: warmup {args.warmup}, steps {args.steps}")
     dres = run_decode(moa, workloads, torch, args.workload, args.steps, args.warmup)
@@ -302,7 +315,9 @@ def main():
                 "bytes_per_step": step_bytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": counter_traffic(), "kernel": f"decode_kernel<{w.head_dim}>",
+                     "traffic": counter_traffic(),
+                     "kernel": f"moa_decode = decode_kernel<{w.head_dim}> + "
+                               f"decode_combine_kernel<{w.head_dim}>",
                      "algorithmic_bytes_per_launch": kbytes,
                      "avg_launch_ms": round(dres["decode_ms"], 4)},
     }

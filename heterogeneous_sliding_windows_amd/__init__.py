@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libmoa.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is not built; run `python -m heterogeneous_sliding_windows_amd.build` "
+        f"{LIB_PATH} is not built; run `python heterogeneous_sliding_windows_amd/build.py` "
         "(or __graft_entry__.build()) first")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -243,9 +243,9 @@ class Plan:
                 torch.zeros(self.cache_elems, dtype=self._torch_dtype(), device="cuda"))
 
     def new_workspace(self):
-        """Zero-filled decode workspace (its tickets must start at zero)."""
+        """Decode workspace (scratch; no initial contents required)."""
         import torch
-        return torch.zeros(self.workspace_bytes, dtype=torch.uint8, device="cuda")
+        return torch.empty(self.workspace_bytes, dtype=torch.uint8, device="cuda")
 
     def close(self):
         if self._h is not None:

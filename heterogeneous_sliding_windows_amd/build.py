@@ -1,7 +1,9 @@
 """Build libmoa.so (gfx950) in the package directory with hipcc.
 
-    python -m heterogeneous_sliding_windows_amd.build [-v]
+    python heterogeneous_sliding_windows_amd/build.py [-v]
 
+Run by file path (not as a module): the package itself refuses to import
+until the library exists.
 Every call recompiles all sources.  Objects go to _build/ at the repository
 root; the shared library lands next to this file, where the binding loads it.
 """

@@ -7,7 +7,7 @@
 // head-specific KV cache; blog digest section 5: static KV cache).
 //
 // The step is bound by HBM bandwidth: every K and V element of every ring is
-// read once.  One kernel launch does the whole step:
+// read once.  Design:
 //  * one workgroup (4 waves) per chunk of up to kDecodeChunk slots of one
 //    (sequence, KV head); each wave streams 256 slots in blocks of 32;
 //  * S^T = K Q^T and O^T += V^T P^T run on the 16x16x32 bf16 matrix cores
@@ -22,9 +22,12 @@
 //  * online softmax per head (running max and sum, exp2 with the scale
 //    folded in); the four waves merge in LDS;
 //  * a head with one chunk writes its output directly; otherwise each chunk
-//    writes (max, sum, o[D]) to the workspace and takes a ticket, and the
-//    last chunk of the (sequence, KV head) merges all partials in chunk order
-//    (deterministic) and resets the ticket for the next call.
+//    writes (max, sum, o[D]) to the workspace and a second, small kernel
+//    merges the partials of every (sequence, KV head) in chunk order
+//    (deterministic).  The kernel boundary publishes the partials to every
+//    XCD; a per-workgroup device-scope fence instead would write back the
+//    whole L2 of the XCD once per chunk, which costs far more than the
+//    second launch.
 
 #include "moa_device.h"
 #include "moa_internal.h"
@@ -41,14 +44,13 @@ __global__ __launch_bounds__(256) void decode_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
     const int4* __restrict__ chunks, const int2* __restrict__ head_chunks,
     const int32_t* __restrict__ span, const int64_t* __restrict__ offset, int64_t slots,
-    int n_chunks, int Hq, int Hkv, int G, float scale_log2, bf16* __restrict__ o,
-    int* __restrict__ counters, float* __restrict__ ws_o, float2* __restrict__ ws_ml) {
+    int n_chunks, int Hq, int G, float scale_log2, bf16* __restrict__ o,
+    float* __restrict__ ws_o, float2* __restrict__ ws_ml) {
   constexpr int KS = D / 32;  // k-steps of the Q.K product
   constexpr int VT = D / 16;  // 16-dim tiles of the output
   __shared__ float sh_o[kWaves][D][17];
   __shared__ float sh_m[kWaves][16];
   __shared__ float sh_l[kWaves][16];
-  __shared__ int sh_last;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -197,8 +199,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
     return;
   }
 
-  // ---- split-K: publish this chunk's partial; the last chunk of the
-  // (sequence, KV head) to finish merges all of them.
+  // ---- split-K: publish this chunk's partial for the combine kernel
   if (g_ok) {
     float* wrow = ws_o + ((int64_t)part * G + g) * D + dgrp * DPT;
 #pragma unroll
@@ -206,24 +207,31 @@ __global__ __launch_bounds__(256) void decode_kernel(
       *reinterpret_cast<float4*>(wrow + i) = make_float4(out[i], out[i + 1], out[i + 2], out[i + 3]);
     if (dgrp == 0) ws_ml[(int64_t)part * G + g] = make_float2(m_tot, l_tot);
   }
-  __threadfence();  // release this chunk's partial device-wide
-  __syncthreads();
-  int* ticket = counters + b * Hkv + h;
-  if (tid == 0) sh_last = atomicAdd(ticket, 1) == n_head_chunks - 1;
-  __syncthreads();
-  if (!sh_last) return;
-  __threadfence();  // acquire the other chunks' partials
-  if (tid == 0) *ticket = 0;  // ready for the next call on this workspace
-  if (!g_ok) return;
+}
 
-  // online merge over the chunks of this head, in chunk order
-  const int64_t part0 = (int64_t)b * n_chunks + head_chunks[h].x;
+// Merge the chunk partials of each (sequence, KV head) with more than one
+// chunk, in chunk order: M = max m_c, L = sum l_c 2^{(m_c - M) c},
+// O = sum o_c 2^{(m_c - M) c} / L.  One workgroup per (sequence, KV head).
+template <int D>
+__global__ __launch_bounds__(256) void decode_combine_kernel(
+    const int2* __restrict__ head_chunks, int n_chunks, int Hq, int Hkv, int G,
+    float scale_log2, const float* __restrict__ ws_o, const float2* __restrict__ ws_ml,
+    bf16* __restrict__ o) {
+  constexpr int DPT = D / 16;
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x / Hkv;
+  const int h = blockIdx.x - b * Hkv;
+  const int2 hc = head_chunks[h];
+  const int g = tid >> 4;
+  const int dgrp = tid & 15;
+  if (hc.y <= 1 || g >= G) return;
+  const int64_t part0 = (int64_t)b * n_chunks + hc.x;
   float M = -INFINITY, L = 0.f;
   float a[DPT];
 #pragma unroll
   for (int i = 0; i < DPT; ++i) a[i] = 0.f;
 #pragma unroll 4
-  for (int c = 0; c < n_head_chunks; ++c) {
+  for (int c = 0; c < hc.y; ++c) {
     const int64_t pc = (part0 + c) * G + g;
     const float2 ml = ws_ml[pc];
     float x[DPT];
@@ -241,6 +249,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
     for (int i = 0; i < DPT; ++i) a[i] = a[i] * sa + x[i] * sb;
   }
   const float inv = 1.f / L;
+  bf16* orow = o + ((int64_t)b * Hq + (int64_t)h * G + g) * D + dgrp * DPT;
 #pragma unroll
   for (int i = 0; i < DPT; ++i) orow[i] = (bf16)(a[i] * inv);
 }
@@ -254,8 +263,13 @@ hipError_t launch(const moa_plan& p, const void* q, const void* kc, const void* 
   hipLaunchKernelGGL(decode_kernel<D>, dim3((unsigned)parts), dim3(256), 0, s,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(kc),
                      static_cast<const bf16*>(vc), p.dev.decode_chunks, p.dev.head_chunks,
-                     p.dev.span, p.dev.offset, p.slots, (int)p.n_chunks, p.Hq, p.Hkv, p.G,
-                     scale_log2, static_cast<bf16*>(o), w.counters, w.o, w.ml);
+                     p.dev.span, p.dev.offset, p.slots, (int)p.n_chunks, p.Hq, p.G,
+                     scale_log2, static_cast<bf16*>(o), w.o, w.ml);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !p.any_split) return e;
+  hipLaunchKernelGGL(decode_combine_kernel<D>, dim3((unsigned)(p.B * p.Hkv)), dim3(256), 0, s,
+                     p.dev.head_chunks, (int)p.n_chunks, p.Hq, p.Hkv, p.G, scale_log2, w.o, w.ml,
+                     static_cast<bf16*>(o));
   return hipGetLastError();
 }
 

@@ -130,6 +130,7 @@ void build_decode_chunks(moa_plan* p) {
   for (int32_t h = 0; h < p->Hkv; ++h) {
     const int32_t s = p->span[h];
     const int32_t cnt = (s + c - 1) / c;
+    p->any_split |= cnt > 1;
     p->head_chunks[2 * h + 0] = idx;
     p->head_chunks[2 * h + 1] = cnt;
     for (int32_t k = 0; k < cnt; ++k) {

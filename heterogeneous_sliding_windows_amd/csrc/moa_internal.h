@@ -40,6 +40,7 @@ struct moa_plan {
   std::vector<int32_t> head_chunks;       // 2 per KV head (first, count)
   int32_t decode_chunk = moa::kDecodeChunk;
   int64_t n_chunks = 0;                   // chunks per sequence
+  bool any_split = false;                 // some head has more than one chunk
   moa::PlanDevice dev;
 };
 
@@ -56,32 +57,24 @@ hipError_t launch_kv_append(const moa_plan& p, void* kc, void* vc, const void* k
 hipError_t launch_decode_bf16(const moa_plan& p, const void* q, const void* kc,
                               const void* vc, void* o, void* ws, hipStream_t s);
 
-// Workspace layout of the split-K decode: int32 tickets[B * Hkv] (padded to
-// 256 bytes; zero before first use, left zero by every call), then
-// float o[n_parts][G][D], then float2 ml[n_parts][G] (running max, sum),
-// n_parts = B * n_chunks.
+// Workspace layout of the split-K decode: float o[n_parts][G][D], then
+// float2 ml[n_parts][G] (running max, sum), n_parts = B * n_chunks.
 struct DecodeWs {
-  int* counters;
   float* o;
   float2* ml;
 };
 
-inline size_t decode_ws_counter_bytes(const moa_plan& p) {
-  return (((size_t)p.B * (size_t)p.Hkv * sizeof(int)) + 255) & ~(size_t)255;
-}
-
 inline size_t decode_ws_bytes(const moa_plan& p) {
   const size_t parts = (size_t)p.B * (size_t)p.n_chunks;
-  size_t bytes = decode_ws_counter_bytes(p) + parts * (size_t)p.G * ((size_t)p.D + 2) * sizeof(float);
-  return (bytes + 255) & ~(size_t)255;
+  size_t bytes = parts * (size_t)p.G * ((size_t)p.D + 2) * sizeof(float);
+  bytes = (bytes + 255) & ~(size_t)255;
+  return bytes < 256 ? 256 : bytes;
 }
 
 inline DecodeWs decode_ws_layout(const moa_plan& p, void* ws) {
   const size_t parts = (size_t)p.B * (size_t)p.n_chunks;
-  char* base = static_cast<char*>(ws);
   DecodeWs w;
-  w.counters = reinterpret_cast<int*>(base);
-  w.o = reinterpret_cast<float*>(base + decode_ws_counter_bytes(p));
+  w.o = static_cast<float*>(ws);
   w.ml = reinterpret_cast<float2*>(w.o + parts * (size_t)p.G * (size_t)p.D);
   return w;
 }

@@ -127,9 +127,7 @@ int moa_plan_tables(moa_plan_t plan, int32_t* span, int64_t* offset,
 /* Elements in ONE cache pool (K or V): B * slots_per_seq * D.  0 on error. */
 int64_t moa_cache_elems(moa_plan_t plan);
 
-/* Bytes of device workspace moa_decode needs (>= 256).  0 on error.  The
- * workspace must be zero-filled before its first moa_decode call; every
- * completed call leaves it ready for the next (its tickets back at zero). */
+/* Bytes of device workspace moa_decode needs (>= 256).  0 on error. */
 size_t moa_decode_workspace_bytes(moa_plan_t plan);
 
 /* Work-list inspection, for tests.  Prefill items are int32 quadruples
@@ -176,15 +174,15 @@ int moa_kv_append(moa_plan_t plan, void* k_cache, void* v_cache,
  * cache has a fixed size), so head h attends positions pos - S_h + 1 .. pos,
  * which are exactly the S_h slots of its ring.
  *   q [B, Hq, D] (input), o [B, Hq, D] (output), plan dtype MOA_BF16.
- * Split-K, one kernel launch: each head's ring is cut into chunks of at
- * most moa_plan_decode_chunk() slots; a head with one chunk writes o
- * directly, otherwise each chunk writes its partial (max, sum, P.V) to
- * `workspace` and takes a ticket, and the last chunk of the (sequence, KV
- * head) merges the partials in chunk order.  workspace: device memory of at
- * least moa_decode_workspace_bytes bytes, zero-filled before its first use
- * (any plan may reuse it afterwards; calls that overlap on one workspace
- * race).  Errors: MOA_EINVAL (null pointers, pos < N, host-only plan),
- * MOA_EUNSUPPORTED (dtype MOA_F32), MOA_EWORKSPACE. */
+ * Split-K: each head's ring is cut into chunks of at most
+ * moa_plan_decode_chunk() slots; a head with one chunk writes o directly,
+ * otherwise each chunk writes its partial (max, sum, P.V) to `workspace` and
+ * a second kernel merges the partials of every (sequence, KV head) in chunk
+ * order.  workspace: device memory of at least moa_decode_workspace_bytes
+ * bytes; its contents need not be initialised and are scratch afterwards
+ * (calls that overlap on one workspace race).  Errors: MOA_EINVAL (null
+ * pointers, pos < N, host-only plan), MOA_EUNSUPPORTED (dtype MOA_F32),
+ * MOA_EWORKSPACE. */
 int moa_decode(moa_plan_t plan, const void* q, const void* k_cache,
                const void* v_cache, int64_t pos, void* o, void* workspace,
                size_t ws_bytes, void* stream);
