@@ -9,7 +9,7 @@
 // The step is bound by HBM bandwidth: every K and V element of every ring is
 // read once.  Design:
 //  * one workgroup (4 waves) per chunk of up to kDecodeChunk slots of one
-//    (sequence, KV head); each wave streams 256 slots in blocks of 32;
+//    (sequence, KV head); the waves stream interleaved blocks of 32 slots;
 //  * S^T = K Q^T and O^T += V^T P^T run on the 16x16x32 bf16 matrix cores
 //    with the G <= 16 query heads of the KV group on the N dimension, so the
 //    dot products need no cross-lane reduction;
@@ -36,8 +36,6 @@ namespace moa {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kWaveSlots = 256;
-static_assert(kWaves * kWaveSlots == kDecodeChunk, "decode chunk size");
 
 template <int D>
 __global__ __launch_bounds__(256) void decode_kernel(
@@ -65,8 +63,11 @@ __global__ __launch_bounds__(256) void decode_kernel(
   const int h = ch.x, first = ch.y, len = ch.z, n_head_chunks = ch.w;
   const int S = span[h];
   const int64_t ring = (int64_t)b * slots + offset[h];
-  const bf16* kbase = kc + (ring + first) * D;   // K ring rows of this chunk
-  const bf16* vbase = vc + ring * D + first;     // V^T ring: dim d at vbase + d*S
+  // K rows of this chunk and the whole V^T ring of this head; loads past the
+  // chunk's K rows return zero.
+  const __amdgpu_buffer_rsrc_t krs =
+      buffer_rsrc(kc + (ring + first) * D, (uint32_t)len * D * 2);
+  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(vc + ring * D, (uint32_t)(D * S * 2));
 
   // Q^T operand: head col of the group (zero rows beyond G).
   bf16x8 qop[KS];
@@ -80,34 +81,44 @@ __global__ __launch_bounds__(256) void decode_kernel(
   for (int t = 0; t < VT; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  const int w0 = wave * kWaveSlots;
-  const int w1 = min(len, w0 + kWaveSlots);
-  for (int k0 = w0; k0 < w1; k0 += 32) {
+  // The four waves take interleaved 32-slot blocks, so at any time they read
+  // neighbouring slots: both 64-byte halves of each 128-byte line of a V^T
+  // row are requested together and the line is fetched from HBM once.
+  const uint32_t krow_off = (8 * (col >> 2) + (col & 3)) * D * 2 + 16 * quad;
+  const uint32_t vrow_off = ((uint32_t)col * S + first + 8 * quad) * 2;
+  const uint32_t vtile = 16u * (uint32_t)S * 2;   // bytes between 16-dim tiles
+  const int w1 = len;
+  const bool v_aligned = (S & 7) == 0;   // V^T rows start on 16-byte boundaries
+  for (int k0 = 32 * wave; k0 < w1; k0 += 32 * kWaves) {
     // ---- loads: K rows of both key tiles, V^T rows of every dim tile
     bf16x8 kop[2][KS];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int key = k0 + 8 * (col >> 2) + 4 * t + (col & 3);
-      const bool ok = key < w1;
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int s = 0; s < KS; ++s)
-        kop[t][s] = ok ? ld16(kbase + (int64_t)key * D + 32 * s + 8 * quad) : zero_bf16x8();
-    }
+        kop[t][s] = buffer_ld16(krs, krow_off + (uint32_t)(k0 + 4 * t) * D * 2 + 64 * s, 0);
     bf16x8 vop[VT];
-    const int vkey = k0 + 8 * quad;  // first of the lane's 8 slots
-    if (vkey + 8 <= w1) {
+    if (v_aligned) {
 #pragma unroll
-      for (int t = 0; t < VT; ++t) vop[t] = ld16(vbase + (int64_t)(16 * t + col) * S + vkey);
-    } else {
-      // ragged end of the chunk: element-wise, never past the slot range
+      for (int t = 0; t < VT; ++t) vop[t] = buffer_ld16(vrs, vrow_off + 2u * k0, t * vtile);
+      if (k0 + 32 > w1) {
+        // ragged end of the chunk: slots past it belong to other chunks (or lie
+        // past the ring and read as zero); clear them so they cannot reach P.V
 #pragma unroll
-      for (int t = 0; t < VT; ++t) {
-        bf16x8 x = zero_bf16x8();
-        const bf16* row = vbase + (int64_t)(16 * t + col) * S;
-        for (int e = 0; e < 8; ++e)
-          if (vkey + e < w1) x[e] = row[vkey + e];
-        vop[t] = x;
+        for (int t = 0; t < VT; ++t)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (k0 + 8 * quad + e >= w1) vop[t][e] = (bf16)0.f;
       }
+    } else {
+      // S_h not a multiple of 8 (S_h = 1, or S_h = N for such N): V^T rows
+      // are not 16-byte aligned, so read element by element
+      const bf16* vrow = vc + ring * D + (int64_t)col * S + first + k0 + 8 * quad;
+#pragma unroll
+      for (int t = 0; t < VT; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          vop[t][e] = k0 + 8 * quad + e < w1 ? vrow[(int64_t)16 * t * S + e] : (bf16)0.f;
     }
 
     // ---- scores S^T: lane holds head col, slots k0 + 8*quad + 4*t + r

@@ -355,6 +355,13 @@ int moa_decode(moa_plan_t p, const void* q, const void* kc, const void* vc, int6
     return fail(MOA_EINVAL, "moa_decode: pos (%lld) must be >= the prompt length %lld", (long long)pos,
                 (long long)p->N);
   if (p->dtype != MOA_BF16) return fail(MOA_EUNSUPPORTED, "moa_decode supports bfloat16 plans only");
+  {
+    // the decode kernel addresses one head's ring with 32-bit byte offsets
+    int32_t smax = 0;
+    for (int32_t x : p->span) smax = x > smax ? x : smax;
+    if ((int64_t)smax * p->D * 2 >= ((int64_t)1 << 31))
+      return fail(MOA_EUNSUPPORTED, "moa_decode: span %d x head_dim %d exceeds 2 GiB per ring", smax, p->D);
+  }
   const size_t need = moa::decode_ws_bytes(*p);
   if (ws_bytes < need)
     return fail(MOA_EWORKSPACE, "moa_decode: workspace of %zu bytes, %zu needed", ws_bytes, need);

@@ -28,6 +28,17 @@ __device__ __forceinline__ bf16x8 ld16(const bf16* p) {
 
 __device__ __forceinline__ void st16(bf16* p, bf16x8 v) { *reinterpret_cast<bf16x8*>(p) = v; }
 
+// Raw buffer resource over [base, base + bytes): loads at byte offsets at or
+// beyond `bytes` return zero.  Addresses are an SGPR base, an SGPR offset and
+// a 32-bit VGPR offset, so a wave needs one VGPR per access stream.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ bf16x8 buffer_ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
 // 16x16x32 bf16 MFMA: A 16x32 (lane l: row l%16, k 8*(l/16)..+7),
 // B 32x16 (lane l: column l%16, same k), C 16x16 (lane l: rows 4*(l/16)+r,
 // column l%16).

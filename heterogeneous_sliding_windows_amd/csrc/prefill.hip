@@ -20,10 +20,13 @@
 //    scores, converted to bf16, with no data movement;
 //  * K tiles are staged in LDS row-major, V tiles transposed (V^T rows are
 //    the P.V A operand: 8 consecutive keys of one dimension per lane);
-//  * global loads of tile t+1 are in flight while tile t is computed;
+//  * LDS tiles are double-buffered: tile t+1 is stored and tile t+2's
+//    global loads are issued before tile t is computed (one barrier a tile);
 //  * masks are evaluated only on tiles a wave's rows do not fully keep, and a
 //    wave skips tiles none of its rows keep;
-//  * online softmax in fp32 with exp2 and the 1/sqrt(D)*log2(e) scale folded.
+//  * online softmax in fp32 with exp2 and the 1/sqrt(D)*log2(e) scale folded;
+//    O and the row sum are rescaled only when a row's max grows by more than
+//    2^8 (exp2 domain), which most tiles after the first never trigger.
 //
 // f32 kernel (the float32 dtype): 2 threads per query row, each owning half
 // of the head dimension; K/V tiles in LDS; plain FMA arithmetic.
@@ -52,8 +55,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
   constexpr int NKG = 256 / CPR;   // V key groups
   constexpr int KPT = BN / NKG;    // keys per thread in the V transpose
   static_assert(KPT == 2 || KPT == 4, "V transpose");
-  __shared__ __attribute__((aligned(16))) bf16 Ks[BN * KP];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[D * VP];
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2][BN * KP];
+  __shared__ __attribute__((aligned(16))) bf16 Vt[2][D * VP];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -108,16 +111,16 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
       vst[i] = key < N ? ld16(vb + (int64_t)key * D + 8 * vdg) : zero_bf16x8();
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < KPASS; ++i) st16(&Ks[(krow0 + i * RPP) * KP + 8 * kchunk], kst[i]);
+    for (int i = 0; i < KPASS; ++i) st16(&Ks[buf][(krow0 + i * RPP) * KP + 8 * kchunk], kst[i]);
     u32x4 w[KPT];
 #pragma unroll
     for (int i = 0; i < KPT; ++i) w[i] = __builtin_bit_cast(u32x4, vst[i]);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      bf16* dst = &Vt[(8 * vdg + e) * VP + vkg * KPT];
+      bf16* dst = &Vt[buf][(8 * vdg + e) * VP + vkg * KPT];
       if constexpr (KPT == 4) {
         u32x2 pk;
         pk[0] = __builtin_amdgcn_perm(w[1][e >> 1], w[0][e >> 1], sel);
@@ -132,67 +135,81 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
   // key row of MFMA row l32 in each 32-key tile (see the file comment)
   const int kperm = 16 * (l32 >> 4) + 8 * ((l32 >> 2) & 1) + 4 * ((l32 >> 3) & 1) + (l32 & 3);
 
+  // Double-buffered tiles: tile kt+1 is stored to LDS and tile kt+2's global
+  // loads are issued before tile kt is computed, so each load has a whole
+  // compute period to arrive; one barrier per tile.
   load_tile(kt_lo);
+  store_tile(0);
+  if (kt_lo < kt_hi) load_tile(kt_lo + 1);
+  __syncthreads();
   for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (kt < kt_hi) load_tile(kt + 1);
+    const int buf = (kt - kt_lo) & 1;
+    if (kt < kt_hi) {
+      store_tile(buf ^ 1);
+      if (kt + 1 < kt_hi) load_tile(kt + 2);
+    }
 
     const int j0 = kt * BN;
     const bool active = iw0 < N && j0 <= iw0 + 31 && j0 + BN - 1 >= iw0 - S + 1;
-    if (!active) continue;
-    const bool full = j0 + BN - 1 <= iw0 && j0 >= iw0 + 31 - S + 1 && j0 + BN <= N;
-
-    floatx16 st[2];
+    if (active) {
+      const bool full = j0 + BN - 1 <= iw0 && j0 >= iw0 + 31 - S + 1 && j0 + BN <= N;
+      floatx16 st[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < 2; ++t) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st[t][r] = 0.f;
-      const bf16* krow = &Ks[(32 * t + kperm) * KP + 8 * half];
+        for (int r = 0; r < 16; ++r) st[t][r] = 0.f;
+        const bf16* krow = &Ks[buf][(32 * t + kperm) * KP + 8 * half];
 #pragma unroll
-      for (int s = 0; s < KS; ++s) st[t] = mfma32(ld16(krow + 16 * s), qop[s], st[t]);
-    }
-    // st[t][r] is the score of query my_q and key j0 + 32t + 16(r>>3) + 8half + (r&7)
-    if (!full) {
+        for (int s = 0; s < KS; ++s) st[t] = mfma32(ld16(krow + 16 * s), qop[s], st[t]);
+      }
+      // st[t][r] is the score of query my_q and key j0 + 32t + 16(r>>3) + 8half + (r&7)
+      if (!full) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = j0 + 32 * t + 16 * (r >> 3) + 8 * half + (r & 7);
+            const bool ok = key <= my_q && key >= my_q - S + 1 && key < N;
+            st[t][r] = ok ? st[t][r] : -INFINITY;
+          }
+      }
+      float mx = st[0][0];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[t][r]);
+      mx = wave_max_xor(mx, 32);
+      // Lazy rescale: the reference max m_run moves (and O, l are rescaled)
+      // only when some row's tile max exceeds it by more than 2^8 in the exp2
+      // domain; otherwise p <= 256, harmless in fp32 and bf16.  The final
+      // O / l is unchanged.  (m_run = -inf compares as +inf growth.)
+      if (__ballot((mx - m_run) * scale_log2 > 8.f)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;  // row with no kept key yet
+        const float alpha = fast_exp2((m_run - m_use) * scale_log2);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int t = 0; t < OT; ++t) acc[t] *= alpha;
+      }
+      const float mb = (m_run == -INFINITY ? 0.f : m_run) * scale_log2;
+      float p[2][16];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = j0 + 32 * t + 16 * (r >> 3) + 8 * half + (r & 7);
-          const bool ok = key <= my_q && key >= my_q - S + 1 && key < N;
-          st[t][r] = ok ? st[t][r] : -INFINITY;
+          p[t][r] = fast_exp2(__builtin_fmaf(st[t][r], scale_log2, -mb));
+          l_run += p[t][r];
         }
-    }
-    float mx = st[0][0];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8 pop = to_bf16x8(&p[j >> 1][8 * (j & 1)]);
+        const bf16* vrow = &Vt[buf][l32 * VP + 16 * j + 8 * half];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[t][r]);
-    mx = wave_max_xor(mx, 32);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;  // row with no kept key yet
-    const float alpha = fast_exp2((m_run - m_use) * scale_log2);
-    m_run = m_new;
-    l_run *= alpha;
-#pragma unroll
-    for (int t = 0; t < OT; ++t) acc[t] *= alpha;
-    const float mb = m_use * scale_log2;
-    float p[2][16];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p[t][r] = fast_exp2(__builtin_fmaf(st[t][r], scale_log2, -mb));
-        l_run += p[t][r];
+        for (int t = 0; t < OT; ++t) acc[t] = mfma32(ld16(vrow + 32 * t * VP), pop, acc[t]);
       }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bf16x8 pop = to_bf16x8(&p[j >> 1][8 * (j & 1)]);
-      const bf16* vrow = &Vt[l32 * VP + 16 * j + 8 * half];
-#pragma unroll
-      for (int t = 0; t < OT; ++t) acc[t] = mfma32(ld16(vrow + 32 * t * VP), pop, acc[t]);
     }
+    __syncthreads();
   }
 
   l_run += __shfl_xor(l_run, 32, 64);

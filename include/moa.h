@@ -181,8 +181,8 @@ int moa_kv_append(moa_plan_t plan, void* k_cache, void* v_cache,
  * order.  workspace: device memory of at least moa_decode_workspace_bytes
  * bytes; its contents need not be initialised and are scratch afterwards
  * (calls that overlap on one workspace race).  Errors: MOA_EINVAL (null
- * pointers, pos < N, host-only plan), MOA_EUNSUPPORTED (dtype MOA_F32),
- * MOA_EWORKSPACE. */
+ * pointers, pos < N, host-only plan), MOA_EUNSUPPORTED (dtype MOA_F32, or
+ * a head whose ring reaches 2 GiB: S_h * D * 2 >= 2^31), MOA_EWORKSPACE. */
 int moa_decode(moa_plan_t plan, const void* q, const void* k_cache,
                const void* v_cache, int64_t pos, void* o, void* workspace,
                size_t ws_bytes, void* stream);
