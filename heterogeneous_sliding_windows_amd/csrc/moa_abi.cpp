@@ -321,6 +321,8 @@ int moa_prefill(moa_plan_t p, const void* q, const void* k, const void* v, void*
   int st = check_plan(p, true);
   if (st != MOA_OK) return st;
   if (!q || !k || !v || !o) return fail(MOA_EINVAL, "moa_prefill: q, k, v and o must not be NULL");
+  if (p->N * p->D * (p->dtype == MOA_BF16 ? 2 : 4) >= ((int64_t)1 << 31))
+    return fail(MOA_EUNSUPPORTED, "moa_prefill: one head's K/V (N x head_dim) must stay below 2 GiB");
   if ((st = set_device(p)) != MOA_OK) return st;
   hipError_t e = p->dtype == MOA_BF16
                      ? moa::launch_prefill_bf16(*p, q, k, v, o, (hipStream_t)stream)

@@ -98,18 +98,18 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
   const int vdg = tid / NKG;  // 8-dim group of the V transpose
   const int vkg = tid % NKG;  // key group of the V transpose
 
+  // K and V of this (b, h_kv) as buffer resources: rows at or past N read as
+  // zero, so the staging loads need no per-row predicate.
+  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(kb, (uint32_t)N * D * 2);
+  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(vb, (uint32_t)N * D * 2);
+  const uint32_t koff = (uint32_t)krow0 * D * 2 + 16 * kchunk;
+  const uint32_t voff = (uint32_t)(vkg * KPT) * D * 2 + 16 * vdg;
   auto load_tile = [&](int kt) {
-    const int j0 = kt * BN;
+    const uint32_t tile = (uint32_t)kt * BN * D * 2;
 #pragma unroll
-    for (int i = 0; i < KPASS; ++i) {
-      const int key = j0 + krow0 + i * RPP;
-      kst[i] = key < N ? ld16(kb + (int64_t)key * D + 8 * kchunk) : zero_bf16x8();
-    }
+    for (int i = 0; i < KPASS; ++i) kst[i] = buffer_ld16(krs, koff + i * RPP * D * 2, tile);
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int key = j0 + vkg * KPT + i;
-      vst[i] = key < N ? ld16(vb + (int64_t)key * D + 8 * vdg) : zero_bf16x8();
-    }
+    for (int i = 0; i < KPT; ++i) vst[i] = buffer_ld16(vrs, voff + i * D * 2, tile);
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
@@ -162,6 +162,14 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
 #pragma unroll
         for (int s = 0; s < KS; ++s) st[t] = mfma32(ld16(krow + 16 * s), qop[s], st[t]);
       }
+      // keep four K-fragment reads in flight ahead of the matrix cores
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * KS - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       // st[t][r] is the score of query my_q and key j0 + 32t + 16(r>>3) + 8half + (r&7)
       if (!full) {
 #pragma unroll
@@ -208,6 +216,14 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
 #pragma unroll
         for (int t = 0; t < OT; ++t) acc[t] = mfma32(ld16(vrow + 32 * t * VP), pop, acc[t]);
       }
+      // same for the V^T fragments of the P.V product
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+      for (int i = 0; i < 4 * OT - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
     }
     __syncthreads();
   }

@@ -153,7 +153,8 @@ int32_t moa_plan_decode_chunk(moa_plan_t plan);
  * Blog digest section 2.1 (sliding-window base mask) and project page
  * "Finding 2" (per-head span; the figure keeps a band of the causal matrix).
  * Key tiles outside a head's window are never read.  Errors: MOA_EINVAL for
- * null pointers or a host-only plan; MOA_EHIP if the launch fails. */
+ * null pointers or a host-only plan; MOA_EUNSUPPORTED when one head's K or V
+ * (N * D elements) reaches 2 GiB; MOA_EHIP if the launch fails. */
 int moa_prefill(moa_plan_t plan, const void* q, const void* k, const void* v,
                 void* o, void* stream);
 
