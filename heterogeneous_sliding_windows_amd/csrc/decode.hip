@@ -17,13 +17,17 @@
 //    8*(m/4) + 4*t + m%4; the S^T output then sits in exactly the layout the
 //    P^T operand of the P.V product needs (lane l: head l%16, slots
 //    8*(l/16) .. +7), so scores never move between lanes;
-//  * V rings are dimension-major, so each P.V operand is one 16-byte load of
-//    8 consecutive slots of one dimension;
+//  * V rings are stored in blocks of 32 slots, each block dimension-major
+//    ([D][32]): a P.V operand is one 16-byte load of 8 consecutive slots of one
+//    dimension, and each wave iteration streams one contiguous 8 KB block
+//    (every load instruction covers 1 KB of whole lines, so the V stream is
+//    read with the nontemporal hint; K rows are read as half lines, which the
+//    hint would evict before their second half is used);
 //  * online softmax per head (running max and sum, exp2 with the scale
 //    folded in); the four waves merge in LDS;
 //  * a head with one chunk writes its output directly; otherwise each chunk
 //    writes (max, sum, o[D]) to the workspace and a second, small kernel
-//    merges the partials of every (sequence, KV head) in chunk order
+//    merges the partials of every (sequence, query head) in a fixed order
 //    (deterministic).  The kernel boundary publishes the partials to every
 //    XCD; a per-workgroup device-scope fence instead would write back the
 //    whole L2 of the XCD once per chunk, which costs far more than the
@@ -67,7 +71,8 @@ __global__ __launch_bounds__(256) void decode_kernel(
   // chunk's K rows return zero.
   const __amdgpu_buffer_rsrc_t krs =
       buffer_rsrc(kc + (ring + first) * D, (uint32_t)len * D * 2);
-  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(vc + ring * D, (uint32_t)(D * S * 2));
+  const int R = (S + 31) & ~31;                   // ring pitch (slots)
+  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(vc + ring * D, (uint32_t)(D * R * 2));
 
   // Q^T operand: head col of the group (zero rows beyond G).
   bf16x8 qop[KS];
@@ -85,10 +90,12 @@ __global__ __launch_bounds__(256) void decode_kernel(
   // neighbouring slots: both 64-byte halves of each 128-byte line of a V^T
   // row are requested together and the line is fetched from HBM once.
   const uint32_t krow_off = (8 * (col >> 2) + (col & 3)) * D * 2 + 16 * quad;
-  const uint32_t vrow_off = ((uint32_t)col * S + first + 8 * quad) * 2;
-  const uint32_t vtile = 16u * (uint32_t)S * 2;   // bytes between 16-dim tiles
+  // V^T ring: blocks of 32 slots, each block [D][32] contiguous (8 KB at
+  // D = 128); lane (col, quad) of dim tile t reads row 16t + col, slots
+  // 8*quad .. +7 of the block: one load instruction covers 1 KB contiguous.
+  const uint32_t vlane = ((uint32_t)col * 32 + 8 * quad) * 2;
+  const uint32_t vblk = 32u * D * 2;                // bytes per block
   const int w1 = len;
-  const bool v_aligned = (S & 7) == 0;   // V^T rows start on 16-byte boundaries
   for (int k0 = 32 * wave; k0 < w1; k0 += 32 * kWaves) {
     // ---- loads: K rows of both key tiles, V^T rows of every dim tile
     bf16x8 kop[2][KS];
@@ -98,27 +105,17 @@ __global__ __launch_bounds__(256) void decode_kernel(
       for (int s = 0; s < KS; ++s)
         kop[t][s] = buffer_ld16(krs, krow_off + (uint32_t)(k0 + 4 * t) * D * 2 + 64 * s, 0);
     bf16x8 vop[VT];
-    if (v_aligned) {
+    const uint32_t vbase = (uint32_t)((first + k0) >> 5) * vblk + vlane;
 #pragma unroll
-      for (int t = 0; t < VT; ++t) vop[t] = buffer_ld16(vrs, vrow_off + 2u * k0, t * vtile);
-      if (k0 + 32 > w1) {
-        // ragged end of the chunk: slots past it belong to other chunks (or lie
-        // past the ring and read as zero); clear them so they cannot reach P.V
-#pragma unroll
-        for (int t = 0; t < VT; ++t)
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (k0 + 8 * quad + e >= w1) vop[t][e] = (bf16)0.f;
-      }
-    } else {
-      // S_h not a multiple of 8 (S_h = 1, or S_h = N for such N): V^T rows
-      // are not 16-byte aligned, so read element by element
-      const bf16* vrow = vc + ring * D + (int64_t)col * S + first + k0 + 8 * quad;
+    for (int t = 0; t < VT; ++t) vop[t] = buffer_ld16_nt(vrs, vbase, t * 16 * 32 * 2);
+    if (k0 + 32 > w1) {
+      // ragged end of the segment: slots past it belong to other chunks or to
+      // the ring's padding; clear them so they cannot reach P.V
 #pragma unroll
       for (int t = 0; t < VT; ++t)
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          vop[t][e] = k0 + 8 * quad + e < w1 ? vrow[(int64_t)16 * t * S + e] : (bf16)0.f;
+          if (k0 + 8 * quad + e >= w1) vop[t][e] = (bf16)0.f;
     }
 
     // ---- scores S^T: lane holds head col, slots k0 + 8*quad + 4*t + r
@@ -220,49 +217,76 @@ __global__ __launch_bounds__(256) void decode_kernel(
   }
 }
 
-// Merge the chunk partials of each (sequence, KV head) with more than one
-// chunk, in chunk order: M = max m_c, L = sum l_c 2^{(m_c - M) c},
-// O = sum o_c 2^{(m_c - M) c} / L.  One workgroup per (sequence, KV head).
+// Merge the chunk partials of each (sequence, query head) whose KV head has
+// more than one chunk: M = max m_c, L = sum l_c 2^{(m_c - M) c},
+// O = sum o_c 2^{(m_c - M) c} / L.  One workgroup per (sequence, query head);
+// thread (cg, dg) merges chunks cg, cg + 8, ... for dims 4dg .. 4dg+3 (all
+// loads independent), then the 8 chunk groups merge in LDS in a fixed order.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(
-    const int2* __restrict__ head_chunks, int n_chunks, int Hq, int Hkv, int G,
-    float scale_log2, const float* __restrict__ ws_o, const float2* __restrict__ ws_ml,
-    bf16* __restrict__ o) {
-  constexpr int DPT = D / 16;
+    const int2* __restrict__ head_chunks, int n_chunks, int Hq, int G, float scale_log2,
+    const float* __restrict__ ws_o, const float2* __restrict__ ws_ml, bf16* __restrict__ o) {
+  constexpr int DG = D / 4;          // float4 groups of a row
+  constexpr int CG = 256 / DG;       // chunk groups
+  __shared__ float sh_m[CG], sh_l[CG];
+  __shared__ float4 sh_o[CG][DG];
   const int tid = threadIdx.x;
-  const int b = blockIdx.x / Hkv;
-  const int h = blockIdx.x - b * Hkv;
+  const int bh = blockIdx.x;
+  const int b = bh / Hq;
+  const int hq = bh - b * Hq;
+  const int h = hq / G;
+  const int g = hq - h * G;
   const int2 hc = head_chunks[h];
-  const int g = tid >> 4;
-  const int dgrp = tid & 15;
-  if (hc.y <= 1 || g >= G) return;
+  if (hc.y <= 1) return;
+  const int dg = tid % DG;
+  const int cg = tid / DG;
   const int64_t part0 = (int64_t)b * n_chunks + hc.x;
   float M = -INFINITY, L = 0.f;
-  float a[DPT];
-#pragma unroll
-  for (int i = 0; i < DPT; ++i) a[i] = 0.f;
-#pragma unroll 4
-  for (int c = 0; c < hc.y; ++c) {
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+  for (int c = cg; c < hc.y; c += CG) {
     const int64_t pc = (part0 + c) * G + g;
     const float2 ml = ws_ml[pc];
-    float x[DPT];
-#pragma unroll
-    for (int i = 0; i < DPT; i += 4) {
-      const float4 v4 = *reinterpret_cast<const float4*>(ws_o + pc * D + dgrp * DPT + i);
-      x[i] = v4.x; x[i + 1] = v4.y; x[i + 2] = v4.z; x[i + 3] = v4.w;
-    }
+    const float4 x = *reinterpret_cast<const float4*>(ws_o + pc * D + 4 * dg);
     const float mn = fmaxf(M, ml.x);
     const float sa = fast_exp2((M - mn) * scale_log2);
     const float sb = fast_exp2((ml.x - mn) * scale_log2);
     M = mn;
     L = L * sa + ml.y * sb;
-#pragma unroll
-    for (int i = 0; i < DPT; ++i) a[i] = a[i] * sa + x[i] * sb;
+    a.x = a.x * sa + x.x * sb;
+    a.y = a.y * sa + x.y * sb;
+    a.z = a.z * sa + x.z * sb;
+    a.w = a.w * sa + x.w * sb;
   }
-  const float inv = 1.f / L;
-  bf16* orow = o + ((int64_t)b * Hq + (int64_t)h * G + g) * D + dgrp * DPT;
+  if (dg == 0) {
+    sh_m[cg] = M;   // -inf for a group without chunks
+    sh_l[cg] = L;
+  }
+  sh_o[cg][dg] = a;
+  __syncthreads();
+  if (cg != 0) return;
+  float Mt = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < DPT; ++i) orow[i] = (bf16)(a[i] * inv);
+  for (int i = 0; i < CG; ++i) Mt = fmaxf(Mt, sh_m[i]);
+  float Lt = 0.f;
+  float4 ot = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int i = 0; i < CG; ++i) {
+    const float w = sh_m[i] == -INFINITY ? 0.f : fast_exp2((sh_m[i] - Mt) * scale_log2);
+    const float4 x = sh_o[i][dg];
+    Lt += w * sh_l[i];
+    ot.x += w * x.x;
+    ot.y += w * x.y;
+    ot.z += w * x.z;
+    ot.w += w * x.w;
+  }
+  const float inv = 1.f / Lt;
+  bf16x4 r;
+  r[0] = (bf16)(ot.x * inv);
+  r[1] = (bf16)(ot.y * inv);
+  r[2] = (bf16)(ot.z * inv);
+  r[3] = (bf16)(ot.w * inv);
+  *reinterpret_cast<bf16x4*>(o + ((int64_t)b * Hq + hq) * D + 4 * dg) = r;
 }
 
 template <int D>
@@ -278,8 +302,8 @@ hipError_t launch(const moa_plan& p, const void* q, const void* kc, const void* 
                      scale_log2, static_cast<bf16*>(o), w.o, w.ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !p.any_split) return e;
-  hipLaunchKernelGGL(decode_combine_kernel<D>, dim3((unsigned)(p.B * p.Hkv)), dim3(256), 0, s,
-                     p.dev.head_chunks, (int)p.n_chunks, p.Hq, p.Hkv, p.G, scale_log2, w.o, w.ml,
+  hipLaunchKernelGGL(decode_combine_kernel<D>, dim3((unsigned)(p.B * p.Hq)), dim3(256), 0, s,
+                     p.dev.head_chunks, (int)p.n_chunks, p.Hq, p.G, scale_log2, w.o, w.ml,
                      static_cast<bf16*>(o));
   return hipGetLastError();
 }

@@ -4,8 +4,8 @@
 // append of positions pos0 .. pos0 + n_new - 1 writes only the last
 // min(n_new, S_h) of them (the others would be overwritten within the same
 // call), so no two threads ever write one slot.  K rings are slot-major rows
-// of D elements; V rings are dimension-major (row d holds the S_h slots of
-// dimension d), the layout decode's P.V product reads.  "Mixture of
+// of D elements; V rings are stored in blocks of 32 slots, each block
+// dimension-major ([D][32]), the layout decode's P.V product reads.  "Mixture of
 // Attention" project page, "Demo" step 03: the deployed KV cache has a fixed
 // size per head.
 
@@ -42,7 +42,7 @@ __device__ __forceinline__ void append_k(
 }
 
 // Positions vary fastest across threads so that the transposed stores of
-// neighbouring threads land on neighbouring slots of one V^T row.
+// neighbouring threads land on neighbouring slots of one V^T block row.
 template <typename T, int D>
 __device__ __forceinline__ void append_v(
     T* __restrict__ vc, const T* __restrict__ vn, const int32_t* __restrict__ span,
@@ -65,9 +65,10 @@ __device__ __forceinline__ void append_v(
     const uint4 x = *(reinterpret_cast<const uint4*>(vn + (bh * n_new + t) * D) + c);
     T vals[VEC];
     __builtin_memcpy(vals, &x, 16);
-    T* dst = vc + (b * slots + offset[h]) * D + (int64_t)(c * VEC) * S + slot;
+    T* dst = vc + (b * slots + offset[h]) * D + (slot >> 5) * (32 * D) + (c * VEC) * 32 +
+             (slot & 31);
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) dst[(int64_t)e * S] = vals[e];
+    for (int e = 0; e < VEC; ++e) dst[e * 32] = vals[e];
   }
 }
 

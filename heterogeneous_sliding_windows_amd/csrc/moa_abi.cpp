@@ -181,7 +181,7 @@ int moa_ring_offsets(const int32_t* span, int32_t n_kv_heads, int64_t* offset,
   for (int32_t h = 0; h < n_kv_heads; ++h) {
     if (span[h] < 1) return fail(MOA_EINVAL, "span[%d] = %d must be >= 1", h, span[h]);
     offset[h] = total;
-    total += span[h];
+    total += ((int64_t)span[h] + 31) / 32 * 32;   // ring pitch: span rounded up to 32 slots
   }
   *slots_per_seq = total;
   return MOA_OK;
@@ -361,7 +361,8 @@ int moa_decode(moa_plan_t p, const void* q, const void* kc, const void* vc, int6
     // the decode kernel addresses one head's ring with 32-bit byte offsets
     int32_t smax = 0;
     for (int32_t x : p->span) smax = x > smax ? x : smax;
-    if ((int64_t)smax * p->D * 2 >= ((int64_t)1 << 31))
+    const int64_t pitch = ((int64_t)smax + 31) / 32 * 32;
+    if (pitch * p->D * 2 >= ((int64_t)1 << 31))
       return fail(MOA_EUNSUPPORTED, "moa_decode: span %d x head_dim %d exceeds 2 GiB per ring", smax, p->D);
   }
   const size_t need = moa::decode_ws_bytes(*p);

@@ -39,6 +39,13 @@ __device__ __forceinline__ bf16x8 buffer_ld16(__amdgpu_buffer_rsrc_t r, uint32_t
   return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
 }
 
+
+// Same, with the nontemporal hint: for streams read once whose every load
+// instruction covers whole 128-byte lines.
+__device__ __forceinline__ bf16x8 buffer_ld16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 2));
+}
+
 // 16x16x32 bf16 MFMA: A 16x32 (lane l: row l%16, k 8*(l/16)..+7),
 // B 32x16 (lane l: column l%16, same k), C 16x16 (lane l: rows 4*(l/16)+r,
 // column l%16).

@@ -34,14 +34,17 @@
  *    or workspace must be ordered by the caller.
  *
  * KV cache ("ring pool") layout.  One pool for K and one for V, each of
- * B * slots_per_seq * D elements, slots_per_seq = sum_h S_h.  Head h of
- * sequence b owns slots offset[h] .. offset[h] + S_h - 1, offset being the
- * exclusive prefix sum of the spans.  Absolute position p of head h lives in
- * slot p mod S_h.
+ * B * slots_per_seq * D elements.  Head h owns a ring of S_h slots, stored
+ * with a pitch of R_h = 32 * ceil(S_h / 32) slots (slots S_h .. R_h - 1 are
+ * padding, never read as keys); offset[h] is the exclusive prefix sum of the
+ * pitches and slots_per_seq their sum.  Absolute position p of head h lives
+ * in slot p mod S_h.
  *    K element (b, h, slot, d) at  (b*slots_per_seq + offset[h] + slot)*D + d
- *    V element (b, h, slot, d) at  (b*slots_per_seq + offset[h])*D + d*S_h + slot
- * (V rings are stored dimension-major so that decode's P.V product reads
- * consecutive slots of one dimension as a matrix-core operand.)
+ *    V element (b, h, slot, d) at  (b*slots_per_seq + offset[h])*D
+ *                                  + (slot / 32)*32*D + d*32 + slot % 32
+ * (V rings are stored in blocks of 32 slots, each block dimension-major, so
+ * decode's P.V product reads 8 consecutive slots of one dimension as a
+ * matrix-core operand and streams each block as 8 KB of contiguous memory.)
  */
 #ifndef MOA_H
 #define MOA_H
@@ -99,10 +102,11 @@ typedef struct moa_plan* moa_plan_t;
 int moa_spans(const int64_t* alpha, const double* beta, int32_t n_kv_heads,
               int64_t n_prompt, int32_t* span);
 
-/* Ring offsets: offset[h] = sum of span[0..h-1] (host int64 array of
- * n_kv_heads), *slots_per_seq = sum of all spans.  Project page, "Demo" step
- * 03: a fixed-size cache per head.  Errors: MOA_EINVAL for null pointers,
- * n_kv_heads < 1 or any span < 1. */
+/* Ring offsets: offset[h] = sum of the ring pitches R of heads 0..h-1 (host
+ * int64 array of n_kv_heads), *slots_per_seq = sum of all pitches, with
+ * R = 32 * ceil(span / 32).  Project page, "Demo" step 03: a fixed-size
+ * cache per head.  Errors: MOA_EINVAL for null pointers, n_kv_heads < 1 or
+ * any span < 1. */
 int moa_ring_offsets(const int32_t* span, int32_t n_kv_heads, int64_t* offset,
                      int64_t* slots_per_seq);
 

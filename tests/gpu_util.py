@@ -17,6 +17,11 @@ def f64(t):
     return t.detach().to("cpu", torch.float64).numpy()
 
 
+def ring_pitch(s):
+    """Slots a ring of span s occupies in the pool (include/moa.h: multiple of 32)."""
+    return (int(s) + 31) // 32 * 32
+
+
 def ring_k(pool, plan, b, h):
     """[S_h, D] view of K ring (b, h) in the layout include/moa.h documents."""
     s, d = int(plan.spans[h]), plan.head_dim
@@ -25,10 +30,12 @@ def ring_k(pool, plan, b, h):
 
 
 def ring_v(pool, plan, b, h):
-    """[S_h, D] view of V ring (b, h): stored dimension-major, returned slot-major."""
+    """[S_h, D] copy of V ring (b, h): stored in 32-slot blocks, each [D][32]."""
     s, d = int(plan.spans[h]), plan.head_dim
+    r = ring_pitch(s)
     base = (b * plan.slots_per_seq + int(plan.offsets[h])) * d
-    return pool[base:base + s * d].view(d, s).t()
+    blocks = pool[base:base + r * d].view(r // 32, d, 32)     # [block][dim][slot]
+    return blocks.permute(0, 2, 1).reshape(r, d)[:s]
 
 
 def ring_positions(s, p_last):

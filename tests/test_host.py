@@ -55,11 +55,17 @@ def test_spans_random_doubles(moa):
         assert list(moa.spans(alpha, beta, n)) == list(oracle.spans(alpha, beta, n))
 
 
+def _pitch(s):
+    """Ring pitch of the pool layout (include/moa.h): span rounded up to 32 slots."""
+    return [(int(x) + 31) // 32 * 32 for x in s]
+
+
 def test_ring_offsets_bit_exact(moa):
-    span = np.array([1, 64, 7, 8192, 3, 65536], dtype=np.int32)
+    span = np.array([1, 64, 7, 8192, 3, 65536, 33], dtype=np.int32)
     off, tot = moa.ring_offsets(span)
-    o_off, o_tot = oracle.ring_offsets(span)
+    o_off, o_tot = oracle.ring_offsets(_pitch(span))
     assert list(off) == list(o_off) and tot == o_tot
+    assert all(p >= s and p - s < 32 for p, s in zip(_pitch(span), span))
 
 
 @pytest.mark.parametrize("name", sorted(workloads.WORKLOADS))
@@ -70,7 +76,7 @@ def test_workload_plan_tables(moa, name):
                     dtype=w.dtype, host_only=True)
     s = oracle.spans(alpha, beta, w.n_prompt)
     assert list(plan.spans) == list(s)
-    off, tot = oracle.ring_offsets(s)
+    off, tot = oracle.ring_offsets(_pitch(s))
     assert list(plan.offsets) == list(off) and plan.slots_per_seq == tot
     assert plan.cache_elems == w.batch * tot * w.head_dim
     if name == "c0_prefill":
