@@ -105,9 +105,11 @@ def blas_threads():
 # GPU legs
 # ---------------------------------------------------------------------------
 
-def run_decode(moa, workloads, torch, name, steps, warmup):
+def run_decode(moa, workloads, torch, name, steps, warmup, dense=False):
     w = workloads.WORKLOADS[name]
     alpha, beta = workloads.rules(name)
+    if dense:   # every head keeps the whole prompt: the dense-cache baseline
+        alpha, beta = [w.n_prompt] * w.n_kv_heads, [0.0] * w.n_kv_heads
     plan = moa.Plan(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, alpha, beta)
     log(f"{name}: rings {2 * plan.cache_elems * 2 / 1e9:.2f} GB, {plan.decode_chunks().shape[0]}"
         f" chunks/seq, workspace {plan.workspace_bytes / 1e6:.1f} MB")
@@ -156,9 +158,11 @@ def run_decode(moa, workloads, torch, name, steps, warmup):
     return res
 
 
-def run_prefill(moa, workloads, torch, name, iters, warmup):
+def run_prefill(moa, workloads, torch, name, iters, warmup, dense=False):
     w = workloads.WORKLOADS[name]
     alpha, beta = workloads.rules(name)
+    if dense:   # every head keeps the whole prompt: full causal attention
+        alpha, beta = [w.n_prompt] * w.n_kv_heads, [0.0] * w.n_kv_heads
     plan = moa.Plan(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, alpha, beta)
     dev = torch.device("cuda")
     shp_q = (w.batch, w.n_q_heads, w.n_prompt, w.head_dim)
@@ -255,6 +259,8 @@ def main():
     ap.add_argument("--prefill-iters", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the dense-cache baseline (every span = N) on the same kernels")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times (the "
@@ -322,6 +328,27 @@ def main():
                      "avg_launch_ms": round(dres["decode_ms"], 4)},
     }
 
+    if not args.no_dense:
+        log("dense-cache baseline: same workload, every span = N")
+        dres2 = run_decode(moa, workloads, torch, args.workload, args.steps, args.warmup,
+                           dense=True)
+        dms = dres2["elapsed_ms"] / args.steps
+        alpha, beta = workloads.rules(args.workload)
+        budget = 288 * 10**9
+        b_moa = moa.max_batch(w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, alpha, beta,
+                              "bf16", budget)
+        b_dense = moa.max_batch(w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt,
+                                [w.n_prompt] * w.n_kv_heads, [0.0] * w.n_kv_heads, "bf16", budget)
+        line["dense_baseline"] = {
+            "ms_per_step": round(dms, 4),
+            "tokens_per_s": round(w.batch * args.steps / (dres2["elapsed_ms"] / 1e3), 1),
+            "moa_speedup_equal_batch": round(dms / ms_step, 3),
+            "hbm_GBps": round(decode_kernel_bytes(dres2["plan"]) / (dres2["decode_ms"] / 1e3) / 1e9, 1),
+            "max_batch_288GB": {"moa": b_moa, "dense": b_dense},
+        }
+        log(f"dense: {dms:.3f} ms/step, MoA speedup {dms / ms_step:.2f}x at equal batch; "
+            f"max batch in 288 GB: MoA {b_moa}, dense {b_dense}")
+
     if not args.no_prefill:
         log(f"prefill workload {args.prefill_workload}")
         pres = run_prefill(moa, workloads, torch, args.prefill_workload, args.prefill_iters, 3)
@@ -337,6 +364,14 @@ def main():
                          "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                          "traffic": None, "kernel": f"prefill_bf16_kernel<{pw.head_dim}>"},
         }
+        if not args.no_dense:
+            pd = run_prefill(moa, workloads, torch, args.prefill_workload, args.prefill_iters, 3,
+                             dense=True)
+            line["prefill"]["dense_baseline"] = {
+                "ms": round(pd["ms"], 4),
+                "tflops": round(prefill_flops(pd["plan"]) / (pd["ms"] / 1e3) / 1e12, 2),
+                "moa_speedup": round(pd["ms"] / pres["ms"], 3)}
+            log(f"dense prefill: {pd['ms']:.3f} ms, MoA speedup {pd['ms'] / pres['ms']:.2f}x")
 
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")

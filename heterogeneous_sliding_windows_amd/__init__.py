@@ -38,7 +38,7 @@ DTYPES = {"f32": MOA_F32, "bf16": MOA_BF16}
 
 # Every symbol include/moa.h declares.
 EXPORTS = ("moa_spans", "moa_ring_offsets", "moa_plan_create", "moa_plan_destroy",
-           "moa_plan_tables", "moa_cache_elems", "moa_decode_workspace_bytes",
+           "moa_plan_tables", "moa_cache_elems", "moa_decode_workspace_bytes", "moa_max_batch",
            "moa_plan_prefill_items", "moa_plan_decode_chunks", "moa_plan_decode_chunk",
            "moa_prefill", "moa_kv_append", "moa_decode", "moa_last_error", "moa_version")
 
@@ -63,6 +63,7 @@ _sig = {
     "moa_plan_tables": (ctypes.c_int, [_P, _I32P, _I64P, _I64P]),
     "moa_cache_elems": (ctypes.c_int64, [_P]),
     "moa_decode_workspace_bytes": (ctypes.c_size_t, [_P]),
+    "moa_max_batch": (ctypes.c_int64, [ctypes.POINTER(_Problem), ctypes.c_uint64]),
     "moa_plan_prefill_items": (ctypes.c_int64, [_P, _I32P]),
     "moa_plan_decode_chunks": (ctypes.c_int64, [_P, _I32P]),
     "moa_plan_decode_chunk": (ctypes.c_int32, [_P]),
@@ -127,6 +128,15 @@ def ring_offsets(span):
     _check(_lib.moa_ring_offsets(s.ctypes.data_as(_I32P), len(s), off.ctypes.data_as(_I64P),
                                  ctypes.byref(tot)))
     return off, tot.value
+
+
+def max_batch(n_q_heads, n_kv_heads, head_dim, n_prompt, alpha, beta, dtype, budget_bytes):
+    """Largest batch whose K/V ring pools and decode workspace fit budget_bytes."""
+    a, ap = _i64(alpha)
+    b, bp = _f64(beta)
+    pr = _Problem(1, int(n_q_heads), int(n_kv_heads), int(head_dim), int(n_prompt), ap, bp,
+                  DTYPES[dtype])
+    return _check(_lib.moa_max_batch(ctypes.byref(pr), int(budget_bytes)))
 
 
 def _stream(stream):

@@ -87,33 +87,34 @@ void free_device(moa_plan* p) {
   p->dev = moa::PlanDevice{};
 }
 
-// Prefill work list: every (b, h_q, 128-row query tile) with the range of
-// 64-key tiles holding at least one kept pair.  The union of the windows of
-// rows i0..i1 is the contiguous key range [max(0, i0 - S + 1), i1], so the
-// live tiles form one range.  Sorted by tile count (longest first, so the
-// tail of the launch holds the short items), ties in (bh, q_tile) order.
+// Prefill work list, shared by every sequence of the batch: each
+// (h_q, 128-row query tile) with the range of 64-key tiles holding at least
+// one kept pair.  The union of the windows of rows i0..i1 is the contiguous
+// key range [max(0, i0 - S + 1), i1], so the live tiles form one range.
+// Sorted by tile count (longest first, so the tail of the launch holds the
+// short items), ties in (h_q, q_tile) order.  The launch runs item-major with
+// the sequence index fastest.
 void build_prefill_items(moa_plan* p) {
   const int64_t n_qt = (p->N + moa::kPrefillBM - 1) / moa::kPrefillBM;
-  struct Item { int32_t bh, qt, lo, hi; };
+  struct Item { int32_t h, qt, lo, hi; };
   std::vector<Item> items;
-  items.reserve((size_t)p->B * p->Hq * n_qt);
-  for (int32_t b = 0; b < p->B; ++b)
-    for (int32_t h = 0; h < p->Hq; ++h) {
-      const int64_t s = p->span[h / p->G];
-      for (int64_t qt = 0; qt < n_qt; ++qt) {
-        const int64_t i0 = qt * moa::kPrefillBM;
-        const int64_t i1 = std::min<int64_t>(i0 + moa::kPrefillBM, p->N) - 1;
-        const int64_t j0 = std::max<int64_t>(0, i0 - s + 1);
-        items.push_back({b * p->Hq + h, (int32_t)qt, (int32_t)(j0 / moa::kPrefillBN),
-                         (int32_t)(i1 / moa::kPrefillBN)});
-      }
+  items.reserve((size_t)p->Hq * n_qt);
+  for (int32_t h = 0; h < p->Hq; ++h) {
+    const int64_t s = p->span[h / p->G];
+    for (int64_t qt = 0; qt < n_qt; ++qt) {
+      const int64_t i0 = qt * moa::kPrefillBM;
+      const int64_t i1 = std::min<int64_t>(i0 + moa::kPrefillBM, p->N) - 1;
+      const int64_t j0 = std::max<int64_t>(0, i0 - s + 1);
+      items.push_back({h, (int32_t)qt, (int32_t)(j0 / moa::kPrefillBN),
+                       (int32_t)(i1 / moa::kPrefillBN)});
     }
+  }
   std::stable_sort(items.begin(), items.end(), [](const Item& a, const Item& b) {
     return (a.hi - a.lo) > (b.hi - b.lo);
   });
   p->prefill_items.resize(items.size() * 4);
   for (size_t i = 0; i < items.size(); ++i) {
-    p->prefill_items[4 * i + 0] = items[i].bh;
+    p->prefill_items[4 * i + 0] = items[i].h;
     p->prefill_items[4 * i + 1] = items[i].qt;
     p->prefill_items[4 * i + 2] = items[i].lo;
     p->prefill_items[4 * i + 3] = items[i].hi;
@@ -213,6 +214,8 @@ int moa_plan_create(const moa_problem* pr, uint32_t flags, moa_plan_t* out) {
   const double items = (double)pr->batch * pr->n_q_heads *
                        ((pr->n_prompt + moa::kPrefillBM - 1) / moa::kPrefillBM);
   if (items > 2.0e9) return fail(MOA_EINVAL, "too many prefill tiles for one launch");
+  if ((double)pr->batch * pr->n_kv_heads * (double)pr->n_prompt / 32.0 > 2.0e9)
+    return fail(MOA_EINVAL, "too many decode chunks for one launch");
 
   moa_plan* p = new (std::nothrow) moa_plan;
   if (!p) return fail(MOA_ENOMEM, "host allocation of the plan failed");
@@ -289,6 +292,29 @@ int64_t moa_cache_elems(moa_plan_t p) {
 size_t moa_decode_workspace_bytes(moa_plan_t p) {
   if (check_plan(p, false) != MOA_OK) return 0;
   return moa::decode_ws_bytes(*p);
+}
+
+int64_t moa_max_batch(const moa_problem* pr, uint64_t budget_bytes) {
+  if (!pr) return fail(MOA_EINVAL, "problem must not be NULL");
+  moa_problem one = *pr;
+  one.batch = 1;
+  moa_plan_t p = nullptr;
+  int st = moa_plan_create(&one, MOA_PLAN_HOST_ONLY, &p);
+  if (st != MOA_OK) return st;
+  // bytes(B) = both pools + the decode workspace moa_decode_workspace_bytes
+  // reports for batch B; the largest B with bytes(B) <= budget
+  const uint64_t elem = p->dtype == MOA_BF16 ? 2 : 4;
+  const uint64_t cache = 2ull * (uint64_t)p->slots * (uint64_t)p->D * elem;
+  const uint64_t ws = (uint64_t)p->n_chunks * (uint64_t)p->G * ((uint64_t)p->D + 2) * 4ull;
+  moa_plan_destroy(p);
+  auto bytes = [&](uint64_t b) {
+    uint64_t w = (b * ws + 255) & ~(uint64_t)255;
+    return b * cache + (w < 256 ? 256 : w);
+  };
+  uint64_t b = budget_bytes / (cache + ws);
+  while (b > 0 && bytes(b) > budget_bytes) --b;
+  while (bytes(b + 1) <= budget_bytes) ++b;
+  return (int64_t)b;
 }
 
 int64_t moa_plan_prefill_items(moa_plan_t p, int32_t* out) {

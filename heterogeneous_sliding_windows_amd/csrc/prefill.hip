@@ -7,8 +7,9 @@
 // page, "Finding 2": each head has its own span, and the figure keeps a band
 // of the causal matrix.
 //
-// Work items come from the plan: 128 query rows of one (b, h_q) and the range
-// of 64-key tiles that hold at least one kept pair, longest items first.
+// Work items come from the plan: 128 query rows of one h_q and the range of
+// 64-key tiles that hold at least one kept pair, longest items first; the
+// grid runs every item for every sequence (sequence index fastest).
 // Tiles outside the window are never loaded.
 //
 // bf16 kernel (4 waves, 32 query rows each):
@@ -44,7 +45,7 @@ template <int D>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, const int4* __restrict__ items, const int32_t* __restrict__ span,
-    int Hq, int Hkv, int G, int N, float scale_log2) {
+    int B, int Hq, int Hkv, int G, int N, float scale_log2) {
   constexpr int KS = D / 16;       // k-steps of the Q.K product
   constexpr int OT = D / 32;       // 32-dim tiles of the output
   constexpr int KP = D + 8;        // K tile pitch (elements)
@@ -64,10 +65,11 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
   const int l32 = lane & 31;
   const int half = lane >> 5;
 
-  const int4 it = items[blockIdx.x];
-  const int bh = it.x, qt = it.y, kt_lo = it.z, kt_hi = it.w;
-  const int b = bh / Hq;
-  const int hq = bh - b * Hq;
+  const int item = blockIdx.x / B;
+  const int b = blockIdx.x - item * B;   // sequence index runs fastest
+  const int4 it = items[item];
+  const int hq = it.x, qt = it.y, kt_lo = it.z, kt_hi = it.w;
+  const int bh = b * Hq + hq;
   const int hkv = hq / G;
   const int S = span[hkv];
   const bf16* qb = q + (int64_t)bh * N * D;
@@ -247,16 +249,17 @@ template <int D>
 __global__ __launch_bounds__(256) void prefill_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ o, const int4* __restrict__ items, const int32_t* __restrict__ span,
-    int Hq, int Hkv, int G, int N, float scale_log2) {
+    int B, int Hq, int Hkv, int G, int N, float scale_log2) {
   constexpr int DH = D / 2;
   __shared__ __attribute__((aligned(16))) float Ks[BN * D];
   __shared__ __attribute__((aligned(16))) float Vs[BN * D];
   const int tid = threadIdx.x;
   const int half = tid & 1;
-  const int4 it = items[blockIdx.x];
-  const int bh = it.x, qt = it.y, kt_lo = it.z, kt_hi = it.w;
-  const int b = bh / Hq;
-  const int hq = bh - b * Hq;
+  const int item = blockIdx.x / B;
+  const int b = blockIdx.x - item * B;
+  const int4 it = items[item];
+  const int hq = it.x, qt = it.y, kt_lo = it.z, kt_hi = it.w;
+  const int bh = b * Hq + hq;
   const int hkv = hq / G;
   const int S = span[hkv];
   const float* kb = k + ((int64_t)b * Hkv + hkv) * N * D;
@@ -333,35 +336,35 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
 
 hipError_t launch_prefill_bf16(const moa_plan& p, const void* q, const void* k, const void* v,
                                void* o, hipStream_t s) {
-  const unsigned n_items = (unsigned)(p.prefill_items.size() / 4);
+  const unsigned n_items = (unsigned)(p.prefill_items.size() / 4 * p.B);
   const float scale_log2 = kLog2e / sqrtf((float)p.D);
   if (p.D == 64)
     hipLaunchKernelGGL(prefill_bf16_kernel<64>, dim3(n_items), dim3(256), 0, s,
                        static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                        static_cast<const bf16*>(v), static_cast<bf16*>(o), p.dev.prefill_items,
-                       p.dev.span, p.Hq, p.Hkv, p.G, (int)p.N, scale_log2);
+                       p.dev.span, p.B, p.Hq, p.Hkv, p.G, (int)p.N, scale_log2);
   else
     hipLaunchKernelGGL(prefill_bf16_kernel<128>, dim3(n_items), dim3(256), 0, s,
                        static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                        static_cast<const bf16*>(v), static_cast<bf16*>(o), p.dev.prefill_items,
-                       p.dev.span, p.Hq, p.Hkv, p.G, (int)p.N, scale_log2);
+                       p.dev.span, p.B, p.Hq, p.Hkv, p.G, (int)p.N, scale_log2);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill_f32(const moa_plan& p, const void* q, const void* k, const void* v,
                               void* o, hipStream_t s) {
-  const unsigned n_items = (unsigned)(p.prefill_items.size() / 4);
+  const unsigned n_items = (unsigned)(p.prefill_items.size() / 4 * p.B);
   const float scale_log2 = kLog2e / sqrtf((float)p.D);
   if (p.D == 64)
     hipLaunchKernelGGL(prefill_f32_kernel<64>, dim3(n_items), dim3(256), 0, s,
                        static_cast<const float*>(q), static_cast<const float*>(k),
                        static_cast<const float*>(v), static_cast<float*>(o), p.dev.prefill_items,
-                       p.dev.span, p.Hq, p.Hkv, p.G, (int)p.N, scale_log2);
+                       p.dev.span, p.B, p.Hq, p.Hkv, p.G, (int)p.N, scale_log2);
   else
     hipLaunchKernelGGL(prefill_f32_kernel<128>, dim3(n_items), dim3(256), 0, s,
                        static_cast<const float*>(q), static_cast<const float*>(k),
                        static_cast<const float*>(v), static_cast<float*>(o), p.dev.prefill_items,
-                       p.dev.span, p.Hq, p.Hkv, p.G, (int)p.N, scale_log2);
+                       p.dev.span, p.B, p.Hq, p.Hkv, p.G, (int)p.N, scale_log2);
   return hipGetLastError();
 }
 

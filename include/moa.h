@@ -134,11 +134,22 @@ int64_t moa_cache_elems(moa_plan_t plan);
 /* Bytes of device workspace moa_decode needs (>= 256).  0 on error. */
 size_t moa_decode_workspace_bytes(moa_plan_t plan);
 
+/* KV-memory budget: the largest batch whose two ring pools (K and V) plus the
+ * decode workspace fit in budget_bytes, for `problem` with its batch field
+ * ignored.  Per sequence that is 2 * slots_per_seq * D * element size plus
+ * the decode partials.  A bounded cache lets a larger batch fit (project
+ * page, "Inference speed and memory efficiency"); the same problem with
+ * every span equal to N gives the dense cache's figure.  Returns the batch
+ * (>= 0) or a negative moa_status (the problem is validated as by
+ * moa_plan_create). */
+int64_t moa_max_batch(const moa_problem* problem, uint64_t budget_bytes);
+
 /* Work-list inspection, for tests.  Prefill items are int32 quadruples
- * {b * Hq + h_q, q_tile, kt_lo, kt_hi}: query rows q_tile*128 .. +127 read
- * key tiles kt_lo .. kt_hi (64 keys each), i.e. every tile holding at least
- * one kept (query, key) pair and no other.  Items are in launch order: cost
- * (kt_hi - kt_lo + 1) descending, ties by (b*Hq + h_q, q_tile) ascending.
+ * {h_q, q_tile, kt_lo, kt_hi}, shared by every sequence: query rows
+ * q_tile*128 .. +127 read key tiles kt_lo .. kt_hi (64 keys each), i.e. every
+ * tile holding at least one kept (query, key) pair and no other.  Items are
+ * in launch order: cost (kt_hi - kt_lo + 1) descending, ties by (h_q,
+ * q_tile) ascending; the launch runs each item for all B sequences in turn.
  * Decode chunks are int32 triples {h_kv, first_slot, n_slots} for one
  * sequence, in launch order; each head's ring is cut into chunks of at most
  * moa_plan_decode_chunk() slots.  Pass out = NULL to get the count; the

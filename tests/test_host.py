@@ -22,7 +22,9 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def test_exports_every_declared_symbol(moa):
     with open(os.path.join(ROOT, "include", "moa.h")) as f:
         header = f.read()
-    declared = sorted(set(re.findall(r"\b(moa_[a-z_]+)\s*\(", header)))
+    # function declarations: a return type at the start of a line, then the name
+    declared = sorted(set(re.findall(
+        r"^(?:const\s+)?[a-z_0-9]+\s*\*?\s*(moa_[a-z_0-9]+)\s*\(", header, re.M)))
     assert declared, "no declarations found"
     assert sorted(moa.EXPORTS) == declared
     lib = ctypes.CDLL(moa.LIB_PATH)
@@ -87,14 +89,13 @@ def test_workload_plan_tables(moa, name):
 def _check_prefill_items(plan, n, span_of_q):
     """Each (bh, q_tile) once; [kt_lo, kt_hi] = exactly the live 64-key tiles; LPT order."""
     items = plan.prefill_items()
-    bhq = plan.batch * plan.n_q_heads
     n_qt = (n + 127) // 128
-    assert len(items) == bhq * n_qt
+    assert len(items) == plan.n_q_heads * n_qt
     seen = set()
-    for bh, qt, lo, hi in items:
-        assert (bh, qt) not in seen
-        seen.add((bh, qt))
-        s = span_of_q(bh % plan.n_q_heads)
+    for hq, qt, lo, hi in items:
+        assert (hq, qt) not in seen
+        seen.add((hq, qt))
+        s = span_of_q(hq)
         rows = np.arange(qt * 128, min(qt * 128 + 128, n))
         # brute force: live tiles from the explicit mask rows
         m = oracle.band_mask(s, n)[rows]
@@ -135,8 +136,8 @@ def test_prefill_items_full_size_tables(moa):
         j = np.arange(n)
         rng = np.random.Generator(np.random.PCG64(3))
         for idx in rng.integers(0, len(items), 200):
-            bh, qt, lo, hi = items[idx]
-            sp = int(s[(bh % w.n_q_heads) // g])
+            hq, qt, lo, hi = items[idx]
+            sp = int(s[hq // g])
             r0, r1 = qt * 128, min(qt * 128 + 128, n) - 1
             kept = np.zeros(n, dtype=bool)
             for i in (r0, r1):                   # the band's extreme rows bound the union
@@ -166,6 +167,35 @@ def test_decode_chunks_cover_rings(moa, name):
     assert plan.workspace_bytes >= w.batch * len(ch) * (w.n_q_heads // w.n_kv_heads) * \
         (w.head_dim + 2) * 4
     plan.close()
+
+
+@pytest.mark.parametrize("name", ["c2_decode", "c3_decode", "c4_decode"])
+def test_max_batch_budget(moa, name):
+    """Largest batch whose pools + decode workspace fit: bytes(B) <= budget < bytes(B+1);
+    a dense cache (every span N) fits about density-times fewer sequences."""
+    w = workloads.WORKLOADS[name]
+    alpha, beta = workloads.rules(name)
+
+    def bytes_for(batch, a, b):
+        plan = moa.Plan(batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, a, b,
+                        host_only=True)
+        n = 2 * plan.cache_elems * 2 + plan.workspace_bytes
+        plan.close()
+        return n
+
+    for budget in (10**9, 96 * 10**9, 288 * 10**9):
+        bmax = moa.max_batch(w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, alpha, beta,
+                             "bf16", budget)
+        if bmax > 0:
+            assert bytes_for(bmax, alpha, beta) <= budget
+        assert bytes_for(bmax + 1, alpha, beta) > budget
+    dense = [w.n_prompt] * w.n_kv_heads, [0.0] * w.n_kv_heads
+    b_moa = moa.max_batch(w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, alpha, beta, "bf16",
+                          288 * 10**9)
+    b_dense = moa.max_batch(w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, *dense, "bf16",
+                            288 * 10**9)
+    density = float(np.mean(oracle.spans(alpha, beta, w.n_prompt))) / w.n_prompt
+    assert abs(b_dense / b_moa - density) < 0.02
 
 
 # ---------------------------------------------------------------------------
