@@ -4,9 +4,11 @@
                     [--prefill-workload c1_prefill] [--no-cpu-baseline]
 
 A step is one decode step of the whole batch: the new token's K/V appended
-to every head's ring (moa_kv_append, n_new = 1), then split-K decode
-attention over the rings (moa_decode: a split-K partial kernel and a small
-combine kernel).  The default workload is
+to every head's ring, then split-K decode attention over the rings, both in
+moa_append_decode (a split-K partial kernel that also writes the new rows,
+and a small combine kernel).  The same rings are also stepped with the two
+separate calls (moa_kv_append, then moa_decode), reported beside it.  The
+default workload is
 the Vicuna-7B-shaped decode (B64, H32, D128, prompt 16384, 50 % mean
 density); `value` is decode tokens/s of that batch (B tokens per step) with
 every input resident in HBM.  The same run times the Vicuna-7B-shaped
@@ -59,9 +61,9 @@ def prefill_flops(plan):
 
 
 def decode_kernel_bytes(plan):
-    """K and V ring reads plus q read and o write, bf16."""
+    """K and V ring reads (S_h slots per head, padding excluded) plus q read and o write, bf16."""
     d, b = plan.head_dim, plan.batch
-    return 2 * 2 * d * b * int(plan.slots_per_seq) + 2 * 2 * d * b * plan.n_q_heads
+    return 2 * 2 * d * b * int(np.sum(plan.spans, dtype=np.int64)) + 2 * 2 * d * b * plan.n_q_heads
 
 
 def append_bytes(plan):
@@ -106,6 +108,9 @@ def blas_threads():
 # ---------------------------------------------------------------------------
 
 def run_decode(moa, workloads, torch, name, steps, warmup, dense=False):
+    """Times the decode step both ways on the same rings: "fused" (moa_append_decode, one
+    launch + combine) and "separate" (moa_kv_append, then moa_decode).  Positions run on
+    from one mode to the next, so each step is a real append-then-attend."""
     w = workloads.WORKLOADS[name]
     alpha, beta = workloads.rules(name)
     if dense:   # every head keeps the whole prompt: the dense-cache baseline
@@ -117,7 +122,8 @@ def run_decode(moa, workloads, torch, name, steps, warmup, dense=False):
     kc = workloads.device_normal_(torch.empty(plan.cache_elems, dtype=torch.bfloat16, device=dev), 11)
     vc = workloads.device_normal_(torch.empty(plan.cache_elems, dtype=torch.bfloat16, device=dev), 12)
     ws = plan.new_workspace()
-    total = warmup + steps
+    modes = ("fused", "separate")
+    total = len(modes) * (warmup + steps)
     qs = workloads.device_normal_(torch.empty(total, w.batch, w.n_q_heads, w.head_dim,
                                               dtype=torch.bfloat16, device=dev), 13)
     ks = workloads.device_normal_(torch.empty(total, w.batch, w.n_kv_heads, 1, w.head_dim,
@@ -127,38 +133,50 @@ def run_decode(moa, workloads, torch, name, steps, warmup, dense=False):
     out = torch.empty(w.batch, w.n_q_heads, w.head_dim, dtype=torch.bfloat16, device=dev)
     n = w.n_prompt
     stream = torch.cuda.current_stream()
+    res = dict(plan=plan, w=w)
+    t = 0
+    for mode in modes:
+        def attend(t, mode=mode):
+            if mode == "fused":
+                plan.append_decode(qs[t], kc, vc, ks[t, :, :, 0], vs[t, :, :, 0], n + t, out, ws,
+                                   stream=stream)
+            else:
+                plan.decode(qs[t], kc, vc, n + t, out, ws, stream=stream)
 
-    def step(t):
-        plan.kv_append(kc, vc, ks[t], vs[t], n + t, stream=stream)
-        plan.decode(qs[t], kc, vc, n + t, out, ws, stream=stream)
+        def append(t, mode=mode):
+            if mode == "separate":
+                plan.kv_append(kc, vc, ks[t], vs[t], n + t, stream=stream)
 
-    for t in range(warmup):
-        step(t)
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(steps):
-        t = warmup + i
-        plan.kv_append(kc, vc, ks[t], vs[t], n + t, stream=stream)
-        ev[i][0].record(stream)
-        plan.decode(qs[t], kc, vc, n + t, out, ws, stream=stream)
-        ev[i][1].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    elapsed_ms = t_start.elapsed_time(t_end)
-    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    assert torch.isfinite(out.float()).all(), "non-finite decode output"
-    res = dict(plan=plan, elapsed_ms=elapsed_ms, decode_ms=dec_ms, w=w)
+        for _ in range(warmup):
+            append(t)
+            attend(t)
+            t += 1
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_start.record(stream)
+        for i in range(steps):
+            append(t)
+            ev[i][0].record(stream)
+            attend(t)
+            ev[i][1].record(stream)
+            t += 1
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        res[mode] = dict(elapsed_ms=t_start.elapsed_time(t_end),
+                         decode_ms=float(np.mean([a.elapsed_time(b) for a, b in ev])))
+        assert torch.isfinite(out.float()).all(), "non-finite decode output"
     del kc, vc, ws, qs, ks, vs
     torch.cuda.empty_cache()
     return res
 
 
 def run_prefill(moa, workloads, torch, name, iters, warmup, dense=False):
+    """Median prefill time, and the prompt's handoff to the rings both ways: a separate
+    moa_kv_append(pos0 = 0, n_new = N) and the fused moa_prefill_handoff."""
     w = workloads.WORKLOADS[name]
     alpha, beta = workloads.rules(name)
     if dense:   # every head keeps the whole prompt: full causal attention
@@ -173,23 +191,26 @@ def run_prefill(moa, workloads, torch, name, iters, warmup, dense=False):
     o = torch.empty_like(q)
     kc, vc = plan.new_cache()
     stream = torch.cuda.current_stream()
+
+    def timed(fn, count):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(count)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
     for _ in range(warmup):
         plan.prefill(q, k, v, o, stream=stream)
+        plan.prefill_handoff(q, k, v, o, kc, vc, stream=stream)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(iters)]
-    for a, b in ev:
-        a.record(stream)
-        plan.prefill(q, k, v, o, stream=stream)
-        b.record(stream)
-    h0, h1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    h0.record(stream)
-    plan.kv_append(kc, vc, k, v, 0, stream=stream)       # prompt -> ring handoff
-    h1.record(stream)
-    torch.cuda.synchronize()
+    ms = timed(lambda: plan.prefill(q, k, v, o, stream=stream), iters)
+    handoff_ms = timed(lambda: plan.kv_append(kc, vc, k, v, 0, stream=stream), 5)
+    fused_ms = timed(lambda: plan.prefill_handoff(q, k, v, o, kc, vc, stream=stream), iters)
     assert torch.isfinite(o.float()).all(), "non-finite prefill output"
-    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
-    res = dict(plan=plan, ms=ms, handoff_ms=h0.elapsed_time(h1), w=w)
+    res = dict(plan=plan, ms=ms, handoff_ms=handoff_ms, fused_ms=fused_ms, w=w)
     del q, k, v, o, kc, vc
     torch.cuda.empty_cache()
     return res
@@ -289,13 +310,19 @@ def main():
     log(f"decode workload {args.workload}: warmup {args.warmup}, steps {args.steps}")
     dres = run_decode(moa, workloads, torch, args.workload, args.steps, args.warmup)
     plan, w = dres["plan"], dres["w"]
-    ms_step = dres["elapsed_ms"] / args.steps
-    tokens_s = w.batch * args.steps / (dres["elapsed_ms"] / 1e3)
-    kbytes = decode_kernel_bytes(plan)
-    step_bytes = kbytes + append_bytes(plan)
-    achieved = kbytes / (dres["decode_ms"] / 1e3) / 1e9
-    log(f"decode: {ms_step:.3f} ms/step, kernel {dres['decode_ms']:.3f} ms, "
-        f"{achieved:.0f} GB/s, {tokens_s:.0f} tokens/s")
+    fused, sep = dres["fused"], dres["separate"]
+    ms_step = fused["elapsed_ms"] / args.steps
+    tokens_s = w.batch * args.steps / (fused["elapsed_ms"] / 1e3)
+    # the fused launch reads the rings, q and the new rows, and writes o and the new rows
+    kbytes = decode_kernel_bytes(plan) + append_bytes(plan)
+    step_bytes = kbytes
+    achieved = kbytes / (fused["decode_ms"] / 1e3) / 1e9
+    sep_ms = sep["elapsed_ms"] / args.steps
+    sep_achieved = decode_kernel_bytes(plan) / (sep["decode_ms"] / 1e3) / 1e9
+    log(f"decode (fused append+decode): {ms_step:.3f} ms/step, kernel {fused['decode_ms']:.3f} ms,"
+        f" {achieved:.0f} GB/s, {tokens_s:.0f} tokens/s")
+    log(f"decode (kv_append, then decode): {sep_ms:.3f} ms/step, decode kernel "
+        f"{sep['decode_ms']:.3f} ms, {sep_achieved:.0f} GB/s")
 
     line = {
         "metric": METRIC,
@@ -315,24 +342,31 @@ def main():
                    "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                    "head_dim": w.head_dim, "n_prompt": w.n_prompt,
                    "mean_density": round(float(np.mean(plan.spans)) / w.n_prompt, 4),
-                   "step": "kv_append(1 token/seq) + decode, one layer"},
+                   "step": "moa_append_decode: append of 1 token/seq fused into decode, "
+                           "one layer"},
         "hbm": {"step_GBps": round(step_bytes / (ms_step / 1e3) / 1e9, 1),
                 "step_frac": round(step_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
                 "bytes_per_step": step_bytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": counter_traffic(),
-                     "kernel": f"moa_decode = decode_kernel<{w.head_dim}> + "
+                     "kernel": f"moa_append_decode = decode_kernel<{w.head_dim}, true> + "
                                f"decode_combine_kernel<{w.head_dim}>",
                      "algorithmic_bytes_per_launch": kbytes,
-                     "avg_launch_ms": round(dres["decode_ms"], 4)},
+                     "avg_launch_ms": round(fused["decode_ms"], 4)},
+        "separate_calls": {
+            "step": "moa_kv_append(1 token/seq), then moa_decode",
+            "ms_per_step": round(sep_ms, 4),
+            "tokens_per_s": round(w.batch * args.steps / (sep["elapsed_ms"] / 1e3), 1),
+            "decode_ms": round(sep["decode_ms"], 4),
+            "decode_GBps": round(sep_achieved, 1)},
     }
 
     if not args.no_dense:
         log("dense-cache baseline: same workload, every span = N")
         dres2 = run_decode(moa, workloads, torch, args.workload, args.steps, args.warmup,
                            dense=True)
-        dms = dres2["elapsed_ms"] / args.steps
+        dms = dres2["fused"]["elapsed_ms"] / args.steps
         alpha, beta = workloads.rules(args.workload)
         budget = 288 * 10**9
         b_moa = moa.max_batch(w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, alpha, beta,
@@ -341,9 +375,10 @@ def main():
                                 [w.n_prompt] * w.n_kv_heads, [0.0] * w.n_kv_heads, "bf16", budget)
         line["dense_baseline"] = {
             "ms_per_step": round(dms, 4),
-            "tokens_per_s": round(w.batch * args.steps / (dres2["elapsed_ms"] / 1e3), 1),
+            "tokens_per_s": round(w.batch * args.steps / (dres2["fused"]["elapsed_ms"] / 1e3), 1),
             "moa_speedup_equal_batch": round(dms / ms_step, 3),
-            "hbm_GBps": round(decode_kernel_bytes(dres2["plan"]) / (dres2["decode_ms"] / 1e3) / 1e9, 1),
+            "hbm_GBps": round((decode_kernel_bytes(dres2["plan"]) + append_bytes(dres2["plan"]))
+                              / (dres2["fused"]["decode_ms"] / 1e3) / 1e9, 1),
             "max_batch_288GB": {"moa": b_moa, "dense": b_dense},
         }
         log(f"dense: {dms:.3f} ms/step, MoA speedup {dms / ms_step:.2f}x at equal batch; "
@@ -355,10 +390,12 @@ def main():
         pplan, pw = pres["plan"], pres["w"]
         fl = prefill_flops(pplan)
         tf = fl / (pres["ms"] / 1e3) / 1e12
-        log(f"prefill: {pres['ms']:.3f} ms, {tf:.1f} TFLOP/s, handoff {pres['handoff_ms']:.3f} ms")
+        log(f"prefill: {pres['ms']:.3f} ms, {tf:.1f} TFLOP/s, handoff {pres['handoff_ms']:.3f} ms;"
+            f" fused prefill+handoff {pres['fused_ms']:.3f} ms")
         line["prefill"] = {
             "workload": f"{pw.name}: {pw.title}", "ms": round(pres["ms"], 4),
             "tflops": round(tf, 2), "handoff_ms": round(pres["handoff_ms"], 4),
+            "fused_prefill_handoff_ms": round(pres["fused_ms"], 4),
             "flops": fl,
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),

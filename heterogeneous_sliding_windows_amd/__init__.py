@@ -40,7 +40,8 @@ DTYPES = {"f32": MOA_F32, "bf16": MOA_BF16}
 EXPORTS = ("moa_spans", "moa_ring_offsets", "moa_plan_create", "moa_plan_destroy",
            "moa_plan_tables", "moa_cache_elems", "moa_decode_workspace_bytes", "moa_max_batch",
            "moa_plan_prefill_items", "moa_plan_decode_chunks", "moa_plan_decode_chunk",
-           "moa_prefill", "moa_kv_append", "moa_decode", "moa_last_error", "moa_version")
+           "moa_prefill", "moa_prefill_handoff", "moa_kv_append", "moa_decode",
+           "moa_append_decode", "moa_last_error", "moa_version")
 
 
 class _Problem(ctypes.Structure):
@@ -68,8 +69,11 @@ _sig = {
     "moa_plan_decode_chunks": (ctypes.c_int64, [_P, _I32P]),
     "moa_plan_decode_chunk": (ctypes.c_int32, [_P]),
     "moa_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P]),
+    "moa_prefill_handoff": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P]),
     "moa_kv_append": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int64, ctypes.c_int64, _P]),
     "moa_decode": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int64, _P, _P, ctypes.c_size_t, _P]),
+    "moa_append_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int64, _P, _P,
+                                         ctypes.c_size_t, _P]),
     "moa_last_error": (ctypes.c_char_p, []),
     "moa_version": (ctypes.c_char_p, []),
 }
@@ -222,6 +226,16 @@ class Plan:
         _check(_lib.moa_prefill(self._h, *args, _stream(stream)))
         return o
 
+    def prefill_handoff(self, q, k, v, o, k_cache, v_cache, stream=None):
+        """prefill() and kv_append(pos0=0) of the whole prompt in one launch."""
+        B, Hq, Hk, N, D = self.batch, self.n_q_heads, self.n_kv_heads, self.n_prompt, self.head_dim
+        args = (self._t(q, (B, Hq, N, D), "q"), self._t(k, (B, Hk, N, D), "k"),
+                self._t(v, (B, Hk, N, D), "v"), self._t(o, (B, Hq, N, D), "o"),
+                self._t(k_cache, self.cache_shape(), "k_cache"),
+                self._t(v_cache, self.cache_shape(), "v_cache"))
+        _check(_lib.moa_prefill_handoff(self._h, *args, _stream(stream)))
+        return o
+
     def kv_append(self, k_cache, v_cache, k_new, v_new, pos0, stream=None):
         B, Hk, D = self.batch, self.n_kv_heads, self.head_dim
         if k_new.dim() != 4:
@@ -233,17 +247,32 @@ class Plan:
                 self._t(v_new, (B, Hk, n_new, D), "v_new"))
         _check(_lib.moa_kv_append(self._h, *args, int(pos0), int(n_new), _stream(stream)))
 
-    def decode(self, q, k_cache, v_cache, pos, o, workspace, stream=None):
+    @staticmethod
+    def _ws(workspace):
         import torch
-        B, Hq, D = self.batch, self.n_q_heads, self.head_dim
         if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" \
                 or not workspace.is_contiguous():
             raise ValueError("workspace must be a contiguous GPU tensor")
+        return ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
+
+    def decode(self, q, k_cache, v_cache, pos, o, workspace, stream=None):
+        B, Hq, D = self.batch, self.n_q_heads, self.head_dim
+        ws, ws_bytes = self._ws(workspace)
         args = (self._t(q, (B, Hq, D), "q"), self._t(k_cache, self.cache_shape(), "k_cache"),
                 self._t(v_cache, self.cache_shape(), "v_cache"))
-        ws_bytes = workspace.numel() * workspace.element_size()
-        _check(_lib.moa_decode(self._h, *args, int(pos), self._t(o, (B, Hq, D), "o"),
-                               ctypes.c_void_p(workspace.data_ptr()), ws_bytes, _stream(stream)))
+        _check(_lib.moa_decode(self._h, *args, int(pos), self._t(o, (B, Hq, D), "o"), ws,
+                               ws_bytes, _stream(stream)))
+        return o
+
+    def append_decode(self, q, k_cache, v_cache, k_new, v_new, pos, o, workspace, stream=None):
+        """kv_append(pos, one token) and decode(pos) in one launch (k_new, v_new [B, Hkv, D])."""
+        B, Hq, Hk, D = self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim
+        ws, ws_bytes = self._ws(workspace)
+        args = (self._t(q, (B, Hq, D), "q"), self._t(k_cache, self.cache_shape(), "k_cache"),
+                self._t(v_cache, self.cache_shape(), "v_cache"),
+                self._t(k_new, (B, Hk, D), "k_new"), self._t(v_new, (B, Hk, D), "v_new"))
+        _check(_lib.moa_append_decode(self._h, *args, int(pos), self._t(o, (B, Hq, D), "o"), ws,
+                                      ws_bytes, _stream(stream)))
         return o
 
     def new_cache(self):

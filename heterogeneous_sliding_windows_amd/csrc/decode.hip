@@ -32,6 +32,17 @@
 //    XCD; a per-workgroup device-scope fence instead would write back the
 //    whole L2 of the XCD once per chunk, which costs far more than the
 //    second launch.
+//
+// Fused append (APPEND = true): the new token's key and value go to slot
+// pos mod S_h.  The partial kernel never reads them from the ring: inside
+// the streaming loop that slot is dropped (score -inf, value zero), and after
+// the loop wave 0 of the chunk holding it adds the new key and value from
+// k_new/v_new as one more step of its online softmax.  The ring write itself
+// is left to the combine kernel, which runs after the streaming has ended:
+// writes interleaved with the saturated read stream (even whole-line ones)
+// measured several times dearer than the same writes in a phase of their own.
+
+#include <cfloat>
 
 #include "moa_device.h"
 #include "moa_internal.h"
@@ -41,13 +52,14 @@ namespace {
 
 constexpr int kWaves = 4;
 
-template <int D>
+template <int D, bool APPEND>
 __global__ __launch_bounds__(256) void decode_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
     const int4* __restrict__ chunks, const int2* __restrict__ head_chunks,
     const int32_t* __restrict__ span, const int64_t* __restrict__ offset, int64_t slots,
     int n_chunks, int Hq, int G, float scale_log2, bf16* __restrict__ o,
-    float* __restrict__ ws_o, float2* __restrict__ ws_ml) {
+    float* __restrict__ ws_o, float2* __restrict__ ws_ml, const bf16* __restrict__ kn,
+    const bf16* __restrict__ vn, int64_t pos) {
   constexpr int KS = D / 32;  // k-steps of the Q.K product
   constexpr int VT = D / 16;  // 16-dim tiles of the output
   __shared__ float sh_o[kWaves][D][17];
@@ -74,6 +86,24 @@ __global__ __launch_bounds__(256) void decode_kernel(
   const int R = (S + 31) & ~31;                   // ring pitch (slots)
   const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(vc + ring * D, (uint32_t)(D * R * 2));
 
+  // Fused append: chunk-relative block (sub_k0) and slot in it (sub_r) of the
+  // new position; sub_k0 = -1 when the slot lies in another chunk.
+  int sub_k0 = -1, sub_r = 0;
+  const bf16* knew = nullptr;
+  const bf16* vnew = nullptr;
+  if constexpr (APPEND) {
+    // pos mod S in 32-bit arithmetic whenever pos < 2^31
+    const uint64_t up = (uint64_t)pos;
+    const int ns = (up >> 31) == 0 ? (int)((uint32_t)up % (uint32_t)S) : (int)(up % (uint64_t)S);
+    const int rel = ns - first;
+    if (rel >= 0 && rel < len) {
+      sub_k0 = rel & ~31;
+      sub_r = rel & 31;
+    }
+    const int64_t row = ((int64_t)b * (Hq / G) + h) * D;
+    knew = kn + row;
+    vnew = vn + row;
+  }
   // Q^T operand: head col of the group (zero rows beyond G).
   bf16x8 qop[KS];
   const bool head_ok = col < G;
@@ -117,7 +147,6 @@ __global__ __launch_bounds__(256) void decode_kernel(
         for (int e = 0; e < 8; ++e)
           if (k0 + 8 * quad + e >= w1) vop[t][e] = (bf16)0.f;
     }
-
     // ---- scores S^T: lane holds head col, slots k0 + 8*quad + 4*t + r
     floatx4 sc[2];
 #pragma unroll
@@ -132,13 +161,29 @@ __global__ __launch_bounds__(256) void decode_kernel(
       const float x = sc[e >> 2][e & 3];
       sv[e] = (k0 + 8 * quad + e < w1) ? x : -INFINITY;
     }
+    if constexpr (APPEND) {
+      if (k0 == sub_k0 && quad == (sub_r >> 3)) {
+        // the new position's slot still holds the position it replaces:
+        // drop it here; the new key and value are added after the loop
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (e == (sub_r & 7)) {
+            sv[e] = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < VT; ++t) vop[t][e] = (bf16)0.f;
+          }
+      }
+    }
     float bm = sv[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) bm = fmaxf(bm, sv[e]);
     bm = wave_max_xor(bm, 16);
     bm = wave_max_xor(bm, 32);
-    // slot k0 is always valid, so bm is finite
-    const float m_new = fmaxf(m_run, bm);
+    // slot k0 is always valid, so bm is finite, unless it is the dropped
+    // slot of a fused append: then keep the reference finite (p and alpha
+    // are 0 for a block with no kept slot)
+    float m_new = fmaxf(m_run, bm);
+    if constexpr (APPEND) m_new = fmaxf(m_new, -FLT_MAX);
     const float alpha = fast_exp2((m_run - m_new) * scale_log2);
     m_run = m_new;
     l_run *= alpha;
@@ -158,6 +203,34 @@ __global__ __launch_bounds__(256) void decode_kernel(
   // sum over the four lane quarters (each summed its own slots)
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
+
+  if constexpr (APPEND) {
+    if (sub_k0 >= 0 && wave == 0) {
+      // the new key and value, one more online-softmax step of wave 0 (its
+      // reference max is finite: it always streams the chunk's first block)
+      float sc_new = 0.f;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8 kx = ld16(knew + 32 * s + 8 * quad);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sc_new = __builtin_fmaf((float)qop[s][e], (float)kx[e], sc_new);
+      }
+      sc_new += __shfl_xor(sc_new, 16, 64);
+      sc_new += __shfl_xor(sc_new, 32, 64);
+      const float m_new = fmaxf(m_run, sc_new);
+      const float alpha = fast_exp2((m_run - m_new) * scale_log2);
+      const float p = fast_exp2(__builtin_fmaf(sc_new, scale_log2, -m_new * scale_log2));
+      m_run = m_new;
+      l_run = l_run * alpha + p;
+#pragma unroll
+      for (int t = 0; t < VT; ++t) {
+        // acc[t][r] holds dim 16t + 4quad + r of head col
+        const bf16x4 vx = *reinterpret_cast<const bf16x4*>(vnew + 16 * t + 4 * quad);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[t][r] = acc[t][r] * alpha + p * (float)vx[r];
+      }
+    }
+  }
 
   // ---- merge the waves of the workgroup
   if (quad == 0) {
@@ -222,10 +295,16 @@ __global__ __launch_bounds__(256) void decode_kernel(
 // O = sum o_c 2^{(m_c - M) c} / L.  One workgroup per (sequence, query head);
 // thread (cg, dg) merges chunks cg, cg + 8, ... for dims 4dg .. 4dg+3 (all
 // loads independent), then the 8 chunk groups merge in LDS in a fixed order.
-template <int D>
+// With APPEND, the workgroup of the first query head of each KV group also
+// writes the new key and value of (sequence, KV head) into slot pos mod S_h
+// of the rings (the partial kernel has finished reading them).
+template <int D, bool APPEND>
 __global__ __launch_bounds__(256) void decode_combine_kernel(
     const int2* __restrict__ head_chunks, int n_chunks, int Hq, int G, float scale_log2,
-    const float* __restrict__ ws_o, const float2* __restrict__ ws_ml, bf16* __restrict__ o) {
+    const float* __restrict__ ws_o, const float2* __restrict__ ws_ml, bf16* __restrict__ o,
+    const bf16* __restrict__ kn, const bf16* __restrict__ vn, bf16* __restrict__ kc,
+    bf16* __restrict__ vc, const int32_t* __restrict__ span, const int64_t* __restrict__ offset,
+    int64_t slots, int64_t pos) {
   constexpr int DG = D / 4;          // float4 groups of a row
   constexpr int CG = 256 / DG;       // chunk groups
   __shared__ float sh_m[CG], sh_l[CG];
@@ -236,6 +315,18 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
   const int hq = bh - b * Hq;
   const int h = hq / G;
   const int g = hq - h * G;
+  if constexpr (APPEND) {
+    if (g == 0) {
+      const int S = span[h];
+      const uint64_t up = (uint64_t)pos;
+      const int slot = (up >> 31) == 0 ? (int)((uint32_t)up % (uint32_t)S) : (int)(up % (uint64_t)S);
+      const int64_t ring = (int64_t)b * slots + offset[h];
+      const int64_t row = ((int64_t)b * (Hq / G) + h) * D;
+      if (tid < D / 8) st16(kc + (ring + slot) * D + 8 * tid, ld16(kn + row + 8 * tid));
+      if (tid < D)
+        vc[(ring + (slot & ~31)) * D + tid * 32 + (slot & 31)] = vn[row + tid];
+    }
+  }
   const int2 hc = head_chunks[h];
   if (hc.y <= 1) return;
   const int dg = tid % DG;
@@ -289,22 +380,28 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
   *reinterpret_cast<bf16x4*>(o + ((int64_t)b * Hq + hq) * D + 4 * dg) = r;
 }
 
-template <int D>
+template <int D, bool APPEND>
 hipError_t launch(const moa_plan& p, const void* q, const void* kc, const void* vc, void* o,
-                  void* ws, hipStream_t s) {
+                  void* ws, const void* kn, const void* vn, int64_t pos, hipStream_t s) {
   const float scale_log2 = kLog2e / sqrtf((float)D);
   const int64_t parts = (int64_t)p.B * p.n_chunks;
   DecodeWs w = decode_ws_layout(p, ws);
-  hipLaunchKernelGGL(decode_kernel<D>, dim3((unsigned)parts), dim3(256), 0, s,
+  hipLaunchKernelGGL((decode_kernel<D, APPEND>), dim3((unsigned)parts), dim3(256), 0, s,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(kc),
                      static_cast<const bf16*>(vc), p.dev.decode_chunks, p.dev.head_chunks,
                      p.dev.span, p.dev.offset, p.slots, (int)p.n_chunks, p.Hq, p.G,
-                     scale_log2, static_cast<bf16*>(o), w.o, w.ml);
+                     scale_log2, static_cast<bf16*>(o), w.o, w.ml, static_cast<const bf16*>(kn),
+                     static_cast<const bf16*>(vn), pos);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !p.any_split) return e;
-  hipLaunchKernelGGL(decode_combine_kernel<D>, dim3((unsigned)(p.B * p.Hq)), dim3(256), 0, s,
-                     p.dev.head_chunks, (int)p.n_chunks, p.Hq, p.G, scale_log2, w.o, w.ml,
-                     static_cast<bf16*>(o));
+  // the combine runs when some head is split, and always for a fused append
+  // (it writes the new rows)
+  if (e != hipSuccess || (!p.any_split && !APPEND)) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<D, APPEND>), dim3((unsigned)(p.B * p.Hq)), dim3(256),
+                     0, s, p.dev.head_chunks, (int)p.n_chunks, p.Hq, p.G, scale_log2, w.o, w.ml,
+                     static_cast<bf16*>(o), static_cast<const bf16*>(kn),
+                     static_cast<const bf16*>(vn), const_cast<bf16*>(static_cast<const bf16*>(kc)),
+                     const_cast<bf16*>(static_cast<const bf16*>(vc)), p.dev.span, p.dev.offset,
+                     p.slots, pos);
   return hipGetLastError();
 }
 
@@ -312,7 +409,15 @@ hipError_t launch(const moa_plan& p, const void* q, const void* kc, const void* 
 
 hipError_t launch_decode_bf16(const moa_plan& p, const void* q, const void* kc, const void* vc,
                               void* o, void* ws, hipStream_t s) {
-  return p.D == 64 ? launch<64>(p, q, kc, vc, o, ws, s) : launch<128>(p, q, kc, vc, o, ws, s);
+  return p.D == 64 ? launch<64, false>(p, q, kc, vc, o, ws, nullptr, nullptr, 0, s)
+                   : launch<128, false>(p, q, kc, vc, o, ws, nullptr, nullptr, 0, s);
+}
+
+hipError_t launch_append_decode_bf16(const moa_plan& p, const void* q, void* kc, void* vc,
+                                     const void* kn, const void* vn, int64_t pos, void* o,
+                                     void* ws, hipStream_t s) {
+  return p.D == 64 ? launch<64, true>(p, q, kc, vc, o, ws, kn, vn, pos, s)
+                   : launch<128, true>(p, q, kc, vc, o, ws, kn, vn, pos, s);
 }
 
 }  // namespace moa

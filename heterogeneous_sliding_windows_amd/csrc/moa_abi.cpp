@@ -161,6 +161,44 @@ int set_device(const moa_plan* p) {
   return MOA_OK;
 }
 
+// Checks shared by moa_prefill and moa_prefill_handoff (the plan's device
+// must be current).
+int check_prefill(moa_plan_t p, const void* q, const void* k, const void* v, const void* o,
+                  const char* who) {
+  int st = check_plan(p, true);
+  if (st != MOA_OK) return st;
+  if (!q || !k || !v || !o) return fail(MOA_EINVAL, "%s: q, k, v and o must not be NULL", who);
+  if (p->N * p->D * (p->dtype == MOA_BF16 ? 2 : 4) >= ((int64_t)1 << 31))
+    return fail(MOA_EUNSUPPORTED, "%s: one head's K/V (N x head_dim) must stay below 2 GiB", who);
+  return set_device(p);
+}
+
+// Checks shared by moa_decode and moa_append_decode.
+int check_decode(moa_plan_t p, const void* q, const void* kc, const void* vc, int64_t pos,
+                 const void* o, const void* ws, size_t ws_bytes, const char* who) {
+  int st = check_plan(p, true);
+  if (st != MOA_OK) return st;
+  if (!q || !kc || !vc || !o || !ws)
+    return fail(MOA_EINVAL, "%s: q, caches, o and workspace must not be NULL", who);
+  if (pos < p->N)
+    return fail(MOA_EINVAL, "%s: pos (%lld) must be >= the prompt length %lld", who,
+                (long long)pos, (long long)p->N);
+  if (p->dtype != MOA_BF16) return fail(MOA_EUNSUPPORTED, "%s supports bfloat16 plans only", who);
+  {
+    // the decode kernel addresses one head's ring with 32-bit byte offsets
+    int32_t smax = 0;
+    for (int32_t x : p->span) smax = x > smax ? x : smax;
+    const int64_t pitch = ((int64_t)smax + 31) / 32 * 32;
+    if (pitch * p->D * 2 >= ((int64_t)1 << 31))
+      return fail(MOA_EUNSUPPORTED, "%s: span %d x head_dim %d exceeds 2 GiB per ring", who, smax,
+                  p->D);
+  }
+  const size_t need = moa::decode_ws_bytes(*p);
+  if (ws_bytes < need)
+    return fail(MOA_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", who, ws_bytes, need);
+  return set_device(p);
+}
+
 }  // namespace
 
 extern "C" {
@@ -344,16 +382,20 @@ int32_t moa_plan_decode_chunk(moa_plan_t p) {
 }
 
 int moa_prefill(moa_plan_t p, const void* q, const void* k, const void* v, void* o, void* stream) {
-  int st = check_plan(p, true);
+  int st = check_prefill(p, q, k, v, o, "moa_prefill");
   if (st != MOA_OK) return st;
-  if (!q || !k || !v || !o) return fail(MOA_EINVAL, "moa_prefill: q, k, v and o must not be NULL");
-  if (p->N * p->D * (p->dtype == MOA_BF16 ? 2 : 4) >= ((int64_t)1 << 31))
-    return fail(MOA_EUNSUPPORTED, "moa_prefill: one head's K/V (N x head_dim) must stay below 2 GiB");
-  if ((st = set_device(p)) != MOA_OK) return st;
-  hipError_t e = p->dtype == MOA_BF16
-                     ? moa::launch_prefill_bf16(*p, q, k, v, o, (hipStream_t)stream)
-                     : moa::launch_prefill_f32(*p, q, k, v, o, (hipStream_t)stream);
+  hipError_t e = moa::launch_prefill(*p, q, k, v, o, nullptr, nullptr, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return MOA_OK;
+}
+
+int moa_prefill_handoff(moa_plan_t p, const void* q, const void* k, const void* v, void* o,
+                        void* kc, void* vc, void* stream) {
+  int st = check_prefill(p, q, k, v, o, "moa_prefill_handoff");
+  if (st != MOA_OK) return st;
+  if (!kc || !vc) return fail(MOA_EINVAL, "moa_prefill_handoff: k_cache and v_cache must not be NULL");
+  hipError_t e = moa::launch_prefill(*p, q, k, v, o, kc, vc, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "prefill_handoff launch");
   return MOA_OK;
 }
 
@@ -375,28 +417,24 @@ int moa_kv_append(moa_plan_t p, void* kc, void* vc, const void* kn, const void* 
 
 int moa_decode(moa_plan_t p, const void* q, const void* kc, const void* vc, int64_t pos, void* o,
                void* ws, size_t ws_bytes, void* stream) {
-  int st = check_plan(p, true);
+  int st = check_decode(p, q, kc, vc, pos, o, ws, ws_bytes, "moa_decode");
   if (st != MOA_OK) return st;
-  if (!q || !kc || !vc || !o || !ws)
-    return fail(MOA_EINVAL, "moa_decode: q, caches, o and workspace must not be NULL");
-  if (pos < p->N)
-    return fail(MOA_EINVAL, "moa_decode: pos (%lld) must be >= the prompt length %lld", (long long)pos,
-                (long long)p->N);
-  if (p->dtype != MOA_BF16) return fail(MOA_EUNSUPPORTED, "moa_decode supports bfloat16 plans only");
-  {
-    // the decode kernel addresses one head's ring with 32-bit byte offsets
-    int32_t smax = 0;
-    for (int32_t x : p->span) smax = x > smax ? x : smax;
-    const int64_t pitch = ((int64_t)smax + 31) / 32 * 32;
-    if (pitch * p->D * 2 >= ((int64_t)1 << 31))
-      return fail(MOA_EUNSUPPORTED, "moa_decode: span %d x head_dim %d exceeds 2 GiB per ring", smax, p->D);
-  }
-  const size_t need = moa::decode_ws_bytes(*p);
-  if (ws_bytes < need)
-    return fail(MOA_EWORKSPACE, "moa_decode: workspace of %zu bytes, %zu needed", ws_bytes, need);
-  if ((st = set_device(p)) != MOA_OK) return st;
   hipError_t e = moa::launch_decode_bf16(*p, q, kc, vc, o, ws, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return MOA_OK;
+}
+
+int moa_append_decode(moa_plan_t p, const void* q, void* kc, void* vc, const void* kn,
+                      const void* vn, int64_t pos, void* o, void* ws, size_t ws_bytes,
+                      void* stream) {
+  int st = check_decode(p, q, kc, vc, pos, o, ws, ws_bytes, "moa_append_decode");
+  if (st != MOA_OK) return st;
+  if (!kn || !vn) return fail(MOA_EINVAL, "moa_append_decode: k_new and v_new must not be NULL");
+  if (pos >= ((int64_t)1 << 62))
+    return fail(MOA_EINVAL, "moa_append_decode: pos out of range");
+  hipError_t e =
+      moa::launch_append_decode_bf16(*p, q, kc, vc, kn, vn, pos, o, ws, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "append_decode launch");
   return MOA_OK;
 }
 

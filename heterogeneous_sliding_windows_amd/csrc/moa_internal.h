@@ -47,15 +47,19 @@ struct moa_plan {
 namespace moa {
 
 // Kernel launchers (one per source file).  They assume validated arguments.
-hipError_t launch_prefill_bf16(const moa_plan& p, const void* q, const void* k,
-                               const void* v, void* o, hipStream_t s);
-hipError_t launch_prefill_f32(const moa_plan& p, const void* q, const void* k,
-                              const void* v, void* o, hipStream_t s);
+// Prefill of the plan's dtype; with kc, vc non-null it also writes the
+// prompt's last S_h positions into the rings (the fused handoff).
+hipError_t launch_prefill(const moa_plan& p, const void* q, const void* k, const void* v,
+                          void* o, void* kc, void* vc, hipStream_t s);
 hipError_t launch_kv_append(const moa_plan& p, void* kc, void* vc, const void* kn,
                             const void* vn, int64_t pos0, int64_t n_new,
                             hipStream_t s);
 hipError_t launch_decode_bf16(const moa_plan& p, const void* q, const void* kc,
                               const void* vc, void* o, void* ws, hipStream_t s);
+// Append of one position (pos) fused into the decode launch.
+hipError_t launch_append_decode_bf16(const moa_plan& p, const void* q, void* kc, void* vc,
+                                     const void* kn, const void* vn, int64_t pos, void* o,
+                                     void* ws, hipStream_t s);
 
 // Workspace layout of the split-K decode: float o[n_parts][G][D], then
 // float2 ml[n_parts][G] (running max, sum), n_parts = B * n_chunks.

@@ -31,6 +31,14 @@
 //
 // f32 kernel (the float32 dtype): 2 threads per query row, each owning half
 // of the head dimension; K/V tiles in LDS; plain FMA arithmetic.
+//
+// Fused handoff (RING = true): besides o, the launch writes positions
+// N - S_h .. N - 1 of every (b, h_kv) into the KV rings, as an append of the
+// whole prompt would.  Key tile kt is the diagonal tile of query tile
+// kt*BN/BM, whose item always streams it; the workgroup of the first query
+// head of each KV group (g = 0) stores the rows of its diagonal tiles that the
+// ring keeps, from the staging registers, while staging them to LDS.  Every
+// ring row is therefore written once, and K/V are read from HBM once.
 
 #include "moa_device.h"
 #include "moa_internal.h"
@@ -41,11 +49,12 @@ namespace {
 constexpr int BM = kPrefillBM;
 constexpr int BN = kPrefillBN;
 
-template <int D>
+template <int D, bool RING>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, const int4* __restrict__ items, const int32_t* __restrict__ span,
-    int B, int Hq, int Hkv, int G, int N, float scale_log2) {
+    int B, int Hq, int Hkv, int G, int N, float scale_log2, bf16* __restrict__ kc,
+    bf16* __restrict__ vc, const int64_t* __restrict__ offset, int64_t slots) {
   constexpr int KS = D / 16;       // k-steps of the Q.K product
   constexpr int OT = D / 32;       // 32-dim tiles of the output
   constexpr int KP = D + 8;        // K tile pitch (elements)
@@ -76,6 +85,16 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
   const bf16* kb = k + ((int64_t)b * Hkv + hkv) * N * D;
   const bf16* vb = v + ((int64_t)b * Hkv + hkv) * N * D;
   bf16* ob = o + (int64_t)bh * N * D;
+  // fused handoff: this workgroup's K/V rings (only g = 0 writes them)
+  bf16* kring = nullptr;
+  bf16* vring = nullptr;
+  if constexpr (RING) {
+    if (hq == hkv * G) {
+      const int64_t r0 = ((int64_t)b * slots + offset[hkv]) * D;
+      kring = kc + r0;
+      vring = vc + r0;
+    }
+  }
 
   const int iw0 = qt * BM + wave * 32;  // first query row of this wave
   const int my_q = iw0 + l32;
@@ -113,9 +132,37 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < KPT; ++i) vst[i] = buffer_ld16(vrs, voff + i * D * 2, tile);
   };
-  auto store_tile = [&](int buf) {
+  // store_tile(buf, kt): the staged tile kt to LDS buffer buf.  With the
+  // fused handoff, rows of the query tile's diagonal key tiles that the ring
+  // keeps (positions N - S .. N - 1, slot p mod S) also go to the rings: K
+  // rows as 16-byte stores; V from the transposed registers, 4 (D = 128) or
+  // 2 (D = 64) consecutive slots of one dimension per store when they are
+  // all kept and contiguous in the ring, else one element at a time.
+  auto store_tile = [&](int buf, int kt) {
+    bool ring_now = false;
+    if constexpr (RING)
+      ring_now = kring != nullptr && kt * BN / BM == qt && (kt + 1) * BN > N - S;
 #pragma unroll
     for (int i = 0; i < KPASS; ++i) st16(&Ks[buf][(krow0 + i * RPP) * KP + 8 * kchunk], kst[i]);
+    if constexpr (RING) {
+      if (ring_now) {
+#pragma unroll
+        for (int i = 0; i < KPASS; ++i) {
+          const int p = kt * BN + krow0 + i * RPP;
+          if (p >= N - S && p < N) st16(kring + (int64_t)(p % S) * D + 8 * kchunk, kst[i]);
+        }
+      }
+    }
+    const int vp0 = kt * BN + vkg * KPT;   // first of this thread's V keys
+    bool v_fast = false;
+    bf16* vdst = nullptr;
+    if constexpr (RING) {
+      // p0 is a multiple of KPT; with S a multiple of KPT (or S = N, slot = p)
+      // the KPT slots are consecutive and inside one 32-slot block
+      v_fast = ring_now && vp0 >= N - S && vp0 + KPT - 1 < N && (S % KPT == 0 || S == N);
+      const int slot0 = v_fast ? vp0 % S : 0;
+      vdst = vring + (int64_t)(slot0 >> 5) * (32 * D) + (8 * vdg) * 32 + (slot0 & 31);
+    }
     u32x4 w[KPT];
 #pragma unroll
     for (int i = 0; i < KPT; ++i) w[i] = __builtin_bit_cast(u32x4, vst[i]);
@@ -128,8 +175,25 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
         pk[0] = __builtin_amdgcn_perm(w[1][e >> 1], w[0][e >> 1], sel);
         pk[1] = __builtin_amdgcn_perm(w[3][e >> 1], w[2][e >> 1], sel);
         *reinterpret_cast<u32x2*>(dst) = pk;
+        if (v_fast) *reinterpret_cast<u32x2*>(vdst + 32 * e) = pk;
       } else {
-        *reinterpret_cast<uint32_t*>(dst) = __builtin_amdgcn_perm(w[1][e >> 1], w[0][e >> 1], sel);
+        const uint32_t pk = __builtin_amdgcn_perm(w[1][e >> 1], w[0][e >> 1], sel);
+        *reinterpret_cast<uint32_t*>(dst) = pk;
+        if (v_fast) *reinterpret_cast<uint32_t*>(vdst + 32 * e) = pk;
+      }
+    }
+    if constexpr (RING) {
+      if (ring_now && !v_fast) {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+          const int p = vp0 + i;
+          if (p >= N - S && p < N) {
+            const int slot = p % S;
+            bf16* d1 = vring + (int64_t)(slot >> 5) * (32 * D) + (8 * vdg) * 32 + (slot & 31);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) d1[32 * e] = vst[i][e];
+          }
+        }
       }
     }
   };
@@ -141,13 +205,13 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
   // loads are issued before tile kt is computed, so each load has a whole
   // compute period to arrive; one barrier per tile.
   load_tile(kt_lo);
-  store_tile(0);
+  store_tile(0, kt_lo);
   if (kt_lo < kt_hi) load_tile(kt_lo + 1);
   __syncthreads();
   for (int kt = kt_lo; kt <= kt_hi; ++kt) {
     const int buf = (kt - kt_lo) & 1;
     if (kt < kt_hi) {
-      store_tile(buf ^ 1);
+      store_tile(buf ^ 1, kt + 1);
       if (kt + 1 < kt_hi) load_tile(kt + 2);
     }
 
@@ -245,11 +309,12 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
     }
 }
 
-template <int D>
+template <int D, bool RING>
 __global__ __launch_bounds__(256) void prefill_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ o, const int4* __restrict__ items, const int32_t* __restrict__ span,
-    int B, int Hq, int Hkv, int G, int N, float scale_log2) {
+    int B, int Hq, int Hkv, int G, int N, float scale_log2, float* __restrict__ kc,
+    float* __restrict__ vc, const int64_t* __restrict__ offset, int64_t slots) {
   constexpr int DH = D / 2;
   __shared__ __attribute__((aligned(16))) float Ks[BN * D];
   __shared__ __attribute__((aligned(16))) float Vs[BN * D];
@@ -265,6 +330,16 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
   const float* kb = k + ((int64_t)b * Hkv + hkv) * N * D;
   const float* vb = v + ((int64_t)b * Hkv + hkv) * N * D;
   const int my_q = qt * BM + (tid >> 1);
+  // fused handoff (see the file comment): only g = 0 writes the rings
+  float* kring = nullptr;
+  float* vring = nullptr;
+  if constexpr (RING) {
+    if (hq == hkv * G) {
+      const int64_t r0 = ((int64_t)b * slots + offset[hkv]) * D;
+      kring = kc + r0;
+      vring = vc + r0;
+    }
+  }
 
   float qr[DH];
   const float* qrow = q + ((int64_t)bh * N + (my_q < N ? my_q : 0)) * D + half * DH;
@@ -290,6 +365,18 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
       }
       *reinterpret_cast<float4*>(&Ks[4 * i]) = kx;
       *reinterpret_cast<float4*>(&Vs[4 * i]) = vx;
+      if constexpr (RING) {
+        if (kring != nullptr && kt * BN / BM == qt && key >= N - S && key < N) {
+          const int slot = key % S;
+          const int d = (4 * i) % D;
+          *reinterpret_cast<float4*>(kring + (int64_t)slot * D + d) = kx;
+          float* dst = vring + (int64_t)(slot >> 5) * (32 * D) + d * 32 + (slot & 31);
+          dst[0] = vx.x;
+          dst[32] = vx.y;
+          dst[64] = vx.z;
+          dst[96] = vx.w;
+        }
+      }
     }
     __syncthreads();
     float sc[BN];
@@ -332,39 +419,51 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
         make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv);
 }
 
-}  // namespace
-
-hipError_t launch_prefill_bf16(const moa_plan& p, const void* q, const void* k, const void* v,
-                               void* o, hipStream_t s) {
+template <int D, bool RING>
+void launch_bf16(const moa_plan& p, const void* q, const void* k, const void* v, void* o, void* kc,
+                 void* vc, hipStream_t s) {
   const unsigned n_items = (unsigned)(p.prefill_items.size() / 4 * p.B);
-  const float scale_log2 = kLog2e / sqrtf((float)p.D);
-  if (p.D == 64)
-    hipLaunchKernelGGL(prefill_bf16_kernel<64>, dim3(n_items), dim3(256), 0, s,
-                       static_cast<const bf16*>(q), static_cast<const bf16*>(k),
-                       static_cast<const bf16*>(v), static_cast<bf16*>(o), p.dev.prefill_items,
-                       p.dev.span, p.B, p.Hq, p.Hkv, p.G, (int)p.N, scale_log2);
-  else
-    hipLaunchKernelGGL(prefill_bf16_kernel<128>, dim3(n_items), dim3(256), 0, s,
-                       static_cast<const bf16*>(q), static_cast<const bf16*>(k),
-                       static_cast<const bf16*>(v), static_cast<bf16*>(o), p.dev.prefill_items,
-                       p.dev.span, p.B, p.Hq, p.Hkv, p.G, (int)p.N, scale_log2);
-  return hipGetLastError();
+  const float scale_log2 = kLog2e / sqrtf((float)D);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, RING>), dim3(n_items), dim3(256), 0, s,
+                     static_cast<const bf16*>(q), static_cast<const bf16*>(k),
+                     static_cast<const bf16*>(v), static_cast<bf16*>(o), p.dev.prefill_items,
+                     p.dev.span, p.B, p.Hq, p.Hkv, p.G, (int)p.N, scale_log2,
+                     static_cast<bf16*>(kc), static_cast<bf16*>(vc), p.dev.offset, p.slots);
 }
 
-hipError_t launch_prefill_f32(const moa_plan& p, const void* q, const void* k, const void* v,
-                              void* o, hipStream_t s) {
+template <int D, bool RING>
+void launch_f32(const moa_plan& p, const void* q, const void* k, const void* v, void* o, void* kc,
+                void* vc, hipStream_t s) {
   const unsigned n_items = (unsigned)(p.prefill_items.size() / 4 * p.B);
-  const float scale_log2 = kLog2e / sqrtf((float)p.D);
-  if (p.D == 64)
-    hipLaunchKernelGGL(prefill_f32_kernel<64>, dim3(n_items), dim3(256), 0, s,
-                       static_cast<const float*>(q), static_cast<const float*>(k),
-                       static_cast<const float*>(v), static_cast<float*>(o), p.dev.prefill_items,
-                       p.dev.span, p.B, p.Hq, p.Hkv, p.G, (int)p.N, scale_log2);
-  else
-    hipLaunchKernelGGL(prefill_f32_kernel<128>, dim3(n_items), dim3(256), 0, s,
-                       static_cast<const float*>(q), static_cast<const float*>(k),
-                       static_cast<const float*>(v), static_cast<float*>(o), p.dev.prefill_items,
-                       p.dev.span, p.B, p.Hq, p.Hkv, p.G, (int)p.N, scale_log2);
+  const float scale_log2 = kLog2e / sqrtf((float)D);
+  hipLaunchKernelGGL((prefill_f32_kernel<D, RING>), dim3(n_items), dim3(256), 0, s,
+                     static_cast<const float*>(q), static_cast<const float*>(k),
+                     static_cast<const float*>(v), static_cast<float*>(o), p.dev.prefill_items,
+                     p.dev.span, p.B, p.Hq, p.Hkv, p.G, (int)p.N, scale_log2,
+                     static_cast<float*>(kc), static_cast<float*>(vc), p.dev.offset, p.slots);
+}
+
+}  // namespace
+
+// kc = vc = nullptr: attention only; otherwise also the ring handoff.
+hipError_t launch_prefill(const moa_plan& p, const void* q, const void* k, const void* v, void* o,
+                          void* kc, void* vc, hipStream_t s) {
+  const bool ring = kc != nullptr;
+  if (p.dtype == MOA_BF16) {
+    if (p.D == 64)
+      ring ? launch_bf16<64, true>(p, q, k, v, o, kc, vc, s)
+           : launch_bf16<64, false>(p, q, k, v, o, kc, vc, s);
+    else
+      ring ? launch_bf16<128, true>(p, q, k, v, o, kc, vc, s)
+           : launch_bf16<128, false>(p, q, k, v, o, kc, vc, s);
+  } else {
+    if (p.D == 64)
+      ring ? launch_f32<64, true>(p, q, k, v, o, kc, vc, s)
+           : launch_f32<64, false>(p, q, k, v, o, kc, vc, s);
+    else
+      ring ? launch_f32<128, true>(p, q, k, v, o, kc, vc, s)
+           : launch_f32<128, false>(p, q, k, v, o, kc, vc, s);
+  }
   return hipGetLastError();
 }
 

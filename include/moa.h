@@ -173,6 +173,17 @@ int32_t moa_plan_decode_chunk(moa_plan_t plan);
 int moa_prefill(moa_plan_t plan, const void* q, const void* k, const void* v,
                 void* o, void* stream);
 
+/* Prefill (as moa_prefill) fused with the handoff of the prompt to the KV
+ * rings (as moa_kv_append(pos0 = 0, n_new = N)) in one launch: positions
+ * N - S_h .. N - 1 of every (b, h) go to slot p mod S_h of k_cache/v_cache
+ * (the layout above), read once from k and v while the attention streams
+ * them.  Project page, "Demo" step 03 (the exported rules feed a kernel
+ * with a fixed-size, head-specific cache).  o and the ring contents equal
+ * those of the two separate calls.  k and v must not overlap the caches.
+ * Errors: those of moa_prefill, and MOA_EINVAL for null caches. */
+int moa_prefill_handoff(moa_plan_t plan, const void* q, const void* k, const void* v,
+                        void* o, void* k_cache, void* v_cache, void* stream);
+
 /* Write positions pos0 .. pos0 + n_new - 1 of every (b, h) into the ring
  * pools.  k_new, v_new: [B, Hkv, n_new, D] in the plan's dtype; row t holds
  * position pos0 + t.  Only the last S_h of them are written for head h (the
@@ -202,6 +213,19 @@ int moa_kv_append(moa_plan_t plan, void* k_cache, void* v_cache,
 int moa_decode(moa_plan_t plan, const void* q, const void* k_cache,
                const void* v_cache, int64_t pos, void* o, void* workspace,
                size_t ws_bytes, void* stream);
+
+/* One decode step in one launch: moa_kv_append(pos, n_new = 1) of k_new,
+ * v_new [B, Hkv, D] fused into moa_decode(pos).  The decode chunk that holds
+ * slot pos mod S_h of a head takes the new key and value from k_new/v_new
+ * and writes them to the ring after it has read its slots, so the ring is
+ * read once and no second launch is needed.  Project page, "Demo" step 03
+ * and "Inference speed and memory efficiency" (fixed-size per-head cache,
+ * append then attend).  o and the ring contents afterwards equal those of
+ * the two separate calls.  Same arguments, workspace and errors as
+ * moa_decode, plus MOA_EINVAL for null k_new/v_new or pos >= 2^62. */
+int moa_append_decode(moa_plan_t plan, const void* q, void* k_cache, void* v_cache,
+                      const void* k_new, const void* v_new, int64_t pos, void* o,
+                      void* workspace, size_t ws_bytes, void* stream);
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* moa_last_error(void);

@@ -234,6 +234,10 @@ def test_raw_abi_errors(moa):
     assert lib.moa_spans(None, None, 1, 10, None) == moa.MOA_EINVAL
     assert lib.moa_plan_destroy(None) == moa.MOA_OK
     assert lib.moa_prefill(None, None, None, None, None, None) == moa.MOA_EINVAL
+    assert lib.moa_prefill_handoff(None, None, None, None, None, None, None,
+                                   None) == moa.MOA_EINVAL
+    assert lib.moa_append_decode(None, None, None, None, None, None, 0, None, None, 0,
+                                 None) == moa.MOA_EINVAL
     assert lib.moa_cache_elems(None) == 0
     assert lib.moa_decode_workspace_bytes(None) == 0
     # unknown flag bits
@@ -255,6 +259,12 @@ def test_host_only_plan_refuses_compute(moa):
     assert lib.moa_kv_append(plan._h, dummy, dummy, dummy, dummy, 0, 1, None) == moa.MOA_EINVAL
     assert lib.moa_decode(plan._h, dummy, dummy, dummy, 50, dummy, dummy, 1 << 30,
                           None) == moa.MOA_EINVAL
+    assert lib.moa_prefill_handoff(plan._h, dummy, dummy, dummy, dummy, dummy, dummy,
+                                   None) == moa.MOA_EINVAL
+    assert "HOST_ONLY" in moa.last_error()
+    assert lib.moa_append_decode(plan._h, dummy, dummy, dummy, dummy, dummy, 50, dummy, dummy,
+                                 1 << 30, None) == moa.MOA_EINVAL
+    assert "HOST_ONLY" in moa.last_error()
     plan.close()
 
 
