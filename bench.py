@@ -117,7 +117,7 @@ def run_decode(moa, workloads, torch, name, steps, warmup, dense=False):
         alpha, beta = [w.n_prompt] * w.n_kv_heads, [0.0] * w.n_kv_heads
     plan = moa.Plan(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, alpha, beta)
     log(f"{name}: rings {2 * plan.cache_elems * 2 / 1e9:.2f} GB, {plan.decode_chunks().shape[0]}"
-        f" chunks/seq, workspace {plan.workspace_bytes / 1e6:.1f} MB")
+        f" decode chunks, workspace {plan.workspace_bytes / 1e6:.1f} MB")
     dev = torch.device("cuda")
     kc = workloads.device_normal_(torch.empty(plan.cache_elems, dtype=torch.bfloat16, device=dev), 11)
     vc = workloads.device_normal_(torch.empty(plan.cache_elems, dtype=torch.bfloat16, device=dev), 12)

@@ -37,8 +37,9 @@ STATUS_NAMES = {0: "MOA_OK", -1: "MOA_EINVAL", -2: "MOA_EUNSUPPORTED", -3: "MOA_
 DTYPES = {"f32": MOA_F32, "bf16": MOA_BF16}
 
 # Every symbol include/moa.h declares.
-EXPORTS = ("moa_spans", "moa_ring_offsets", "moa_plan_create", "moa_plan_destroy",
-           "moa_plan_tables", "moa_cache_elems", "moa_decode_workspace_bytes", "moa_max_batch",
+EXPORTS = ("moa_spans", "moa_ring_offsets", "moa_plan_create", "moa_plan_create_ragged",
+           "moa_plan_destroy", "moa_plan_tables", "moa_plan_seq_tables", "moa_cache_elems",
+           "moa_decode_workspace_bytes", "moa_max_batch",
            "moa_plan_prefill_items", "moa_plan_decode_chunks", "moa_plan_decode_chunk",
            "moa_prefill", "moa_prefill_handoff", "moa_kv_append", "moa_decode",
            "moa_append_decode", "moa_last_error", "moa_version")
@@ -60,8 +61,11 @@ _sig = {
     "moa_ring_offsets": (ctypes.c_int, [_I32P, ctypes.c_int32, _I64P, _I64P]),
     "moa_plan_create": (ctypes.c_int, [ctypes.POINTER(_Problem), ctypes.c_uint32,
                                        ctypes.POINTER(_P)]),
+    "moa_plan_create_ragged": (ctypes.c_int, [ctypes.POINTER(_Problem), _I64P, ctypes.c_uint32,
+                                              ctypes.POINTER(_P)]),
     "moa_plan_destroy": (ctypes.c_int, [_P]),
     "moa_plan_tables": (ctypes.c_int, [_P, _I32P, _I64P, _I64P]),
+    "moa_plan_seq_tables": (ctypes.c_int, [_P, _I32P, _I64P, _I64P]),
     "moa_cache_elems": (ctypes.c_int64, [_P]),
     "moa_decode_workspace_bytes": (ctypes.c_size_t, [_P]),
     "moa_max_batch": (ctypes.c_int64, [ctypes.POINTER(_Problem), ctypes.c_uint64]),
@@ -153,10 +157,18 @@ def _stream(stream):
 
 
 class Plan:
-    """A problem (shapes + per-KV-head (alpha, beta) rules) with its tables."""
+    """A problem (shapes + per-KV-head (alpha, beta) rules) with its tables.
+
+    seq_len: optional per-sequence prompt lengths (a ragged batch, left
+    padded to n_prompt = max(seq_len)); see moa_plan_create_ragged.
+    Tables of every plan: seq_spans [B, Hkv], ring_offsets [B, Hkv] (first
+    slot of each ring in the pools), seq_len [B].  A plan without per-sequence
+    lengths also has spans [Hkv], offsets [Hkv] and slots_per_seq (None for a
+    ragged plan).
+    """
 
     def __init__(self, batch, n_q_heads, n_kv_heads, head_dim, n_prompt, alpha, beta,
-                 dtype="bf16", host_only=False):
+                 dtype="bf16", host_only=False, seq_len=None):
         self._h = None
         self.batch, self.n_q_heads, self.n_kv_heads = int(batch), int(n_q_heads), int(n_kv_heads)
         self.head_dim, self.n_prompt, self.dtype = int(head_dim), int(n_prompt), dtype
@@ -170,29 +182,46 @@ class Plan:
         pr = _Problem(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim,
                       self.n_prompt, ap, bp, DTYPES[dtype])
         h = _P()
-        _check(_lib.moa_plan_create(ctypes.byref(pr), MOA_PLAN_HOST_ONLY if host_only else 0,
-                                    ctypes.byref(h)))
+        flags = MOA_PLAN_HOST_ONLY if host_only else 0
+        self.ragged = seq_len is not None
+        if self.ragged:
+            lens, lp = _i64(seq_len)
+            if len(lens) != self.batch:
+                raise ValueError("seq_len needs one entry per sequence")
+            _check(_lib.moa_plan_create_ragged(ctypes.byref(pr), lp, flags, ctypes.byref(h)))
+        else:
+            _check(_lib.moa_plan_create(ctypes.byref(pr), flags, ctypes.byref(h)))
         self._h = h
-        self.spans = np.zeros(self.n_kv_heads, dtype=np.int32)
-        self.offsets = np.zeros(self.n_kv_heads, dtype=np.int64)
-        tot = ctypes.c_int64(0)
-        _check(_lib.moa_plan_tables(h, self.spans.ctypes.data_as(_I32P),
-                                    self.offsets.ctypes.data_as(_I64P), ctypes.byref(tot)))
-        self.slots_per_seq = tot.value
+        self.seq_spans = np.zeros((self.batch, self.n_kv_heads), dtype=np.int32)
+        self.ring_offsets = np.zeros((self.batch, self.n_kv_heads), dtype=np.int64)
+        self.seq_len = np.zeros(self.batch, dtype=np.int64)
+        _check(_lib.moa_plan_seq_tables(h, self.seq_spans.ctypes.data_as(_I32P),
+                                        self.ring_offsets.ctypes.data_as(_I64P),
+                                        self.seq_len.ctypes.data_as(_I64P)))
+        self.spans = self.offsets = self.slots_per_seq = None
+        if not self.ragged:
+            self.spans = np.zeros(self.n_kv_heads, dtype=np.int32)
+            self.offsets = np.zeros(self.n_kv_heads, dtype=np.int64)
+            tot = ctypes.c_int64(0)
+            _check(_lib.moa_plan_tables(h, self.spans.ctypes.data_as(_I32P),
+                                        self.offsets.ctypes.data_as(_I64P), ctypes.byref(tot)))
+            self.slots_per_seq = tot.value
         self.cache_elems = _lib.moa_cache_elems(h)
         self.workspace_bytes = _lib.moa_decode_workspace_bytes(h)
         self.decode_chunk = _lib.moa_plan_decode_chunk(h)
 
     # -- inspection ---------------------------------------------------------
     def prefill_items(self):
+        """[n, 5] int32 {b (-1: every sequence), h_q, q_tile, kt_lo, kt_hi} in launch order."""
         n = _check(_lib.moa_plan_prefill_items(self._h, None))
-        out = np.zeros((n, 4), dtype=np.int32)
+        out = np.zeros((n, 5), dtype=np.int32)
         _check(_lib.moa_plan_prefill_items(self._h, out.ctypes.data_as(_I32P)))
         return out
 
     def decode_chunks(self):
+        """[n, 4] int32 {b, h_kv, first_slot, n_slots} of all sequences in launch order."""
         n = _check(_lib.moa_plan_decode_chunks(self._h, None))
-        out = np.zeros((n, 3), dtype=np.int32)
+        out = np.zeros((n, 4), dtype=np.int32)
         _check(_lib.moa_plan_decode_chunks(self._h, out.ctypes.data_as(_I32P)))
         return out
 

@@ -55,11 +55,11 @@ constexpr int kWaves = 4;
 template <int D, bool APPEND>
 __global__ __launch_bounds__(256) void decode_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
-    const int4* __restrict__ chunks, const int2* __restrict__ head_chunks,
-    const int32_t* __restrict__ span, const int64_t* __restrict__ offset, int64_t slots,
-    int n_chunks, int Hq, int G, float scale_log2, bf16* __restrict__ o,
-    float* __restrict__ ws_o, float2* __restrict__ ws_ml, const bf16* __restrict__ kn,
-    const bf16* __restrict__ vn, int64_t pos) {
+    const int4* __restrict__ chunks, const int32_t* __restrict__ span,
+    const int64_t* __restrict__ ring_off, const int32_t* __restrict__ seq_len, int Npad, int Hq,
+    int G, float scale_log2, bf16* __restrict__ o, float* __restrict__ ws_o,
+    float2* __restrict__ ws_ml, const bf16* __restrict__ kn, const bf16* __restrict__ vn,
+    int64_t pos) {
   constexpr int KS = D / 32;  // k-steps of the Q.K product
   constexpr int VT = D / 16;  // 16-dim tiles of the output
   __shared__ float sh_o[kWaves][D][17];
@@ -72,13 +72,14 @@ __global__ __launch_bounds__(256) void decode_kernel(
   const int col = lane & 15;   // query head within the group
   const int quad = lane >> 4;
 
-  const int part = blockIdx.x;
-  const int b = part / n_chunks;
-  const int ci = part - b * n_chunks;
-  const int4 ch = chunks[ci];
-  const int h = ch.x, first = ch.y, len = ch.z, n_head_chunks = ch.w;
-  const int S = span[h];
-  const int64_t ring = (int64_t)b * slots + offset[h];
+  const int part = blockIdx.x;       // chunk of all sequences' rings
+  const int4 ch = chunks[part];
+  const int bh = ch.x, first = ch.y, len = ch.z, n_head_chunks = ch.w;
+  const int Hkv = Hq / G;
+  const int b = bh / Hkv;
+  const int h = bh - b * Hkv;
+  const int S = span[bh];
+  const int64_t ring = ring_off[bh];
   // K rows of this chunk and the whole V^T ring of this head; loads past the
   // chunk's K rows return zero.
   const __amdgpu_buffer_rsrc_t krs =
@@ -92,17 +93,17 @@ __global__ __launch_bounds__(256) void decode_kernel(
   const bf16* knew = nullptr;
   const bf16* vnew = nullptr;
   if constexpr (APPEND) {
-    // pos mod S in 32-bit arithmetic whenever pos < 2^31
-    const uint64_t up = (uint64_t)pos;
+    // the sequence's own position (left padding), mod S in 32-bit arithmetic
+    // whenever it is below 2^31
+    const uint64_t up = (uint64_t)(pos - (Npad - seq_len[b]));
     const int ns = (up >> 31) == 0 ? (int)((uint32_t)up % (uint32_t)S) : (int)(up % (uint64_t)S);
     const int rel = ns - first;
     if (rel >= 0 && rel < len) {
       sub_k0 = rel & ~31;
       sub_r = rel & 31;
     }
-    const int64_t row = ((int64_t)b * (Hq / G) + h) * D;
-    knew = kn + row;
-    vnew = vn + row;
+    knew = kn + (int64_t)bh * D;
+    vnew = vn + (int64_t)bh * D;
   }
   // Q^T operand: head col of the group (zero rows beyond G).
   bf16x8 qop[KS];
@@ -300,38 +301,38 @@ __global__ __launch_bounds__(256) void decode_kernel(
 // of the rings (the partial kernel has finished reading them).
 template <int D, bool APPEND>
 __global__ __launch_bounds__(256) void decode_combine_kernel(
-    const int2* __restrict__ head_chunks, int n_chunks, int Hq, int G, float scale_log2,
+    const int2* __restrict__ head_chunks, int Hq, int G, float scale_log2,
     const float* __restrict__ ws_o, const float2* __restrict__ ws_ml, bf16* __restrict__ o,
     const bf16* __restrict__ kn, const bf16* __restrict__ vn, bf16* __restrict__ kc,
-    bf16* __restrict__ vc, const int32_t* __restrict__ span, const int64_t* __restrict__ offset,
-    int64_t slots, int64_t pos) {
+    bf16* __restrict__ vc, const int32_t* __restrict__ span, const int64_t* __restrict__ ring_off,
+    const int32_t* __restrict__ seq_len, int Npad, int64_t pos) {
   constexpr int DG = D / 4;          // float4 groups of a row
   constexpr int CG = 256 / DG;       // chunk groups
   __shared__ float sh_m[CG], sh_l[CG];
   __shared__ float4 sh_o[CG][DG];
   const int tid = threadIdx.x;
-  const int bh = blockIdx.x;
-  const int b = bh / Hq;
-  const int hq = bh - b * Hq;
+  const int b = blockIdx.x / Hq;
+  const int hq = blockIdx.x - b * Hq;
   const int h = hq / G;
   const int g = hq - h * G;
+  const int bh = b * (Hq / G) + h;   // (sequence, KV head)
   if constexpr (APPEND) {
     if (g == 0) {
-      const int S = span[h];
-      const uint64_t up = (uint64_t)pos;
+      const int S = span[bh];
+      const uint64_t up = (uint64_t)(pos - (Npad - seq_len[b]));
       const int slot = (up >> 31) == 0 ? (int)((uint32_t)up % (uint32_t)S) : (int)(up % (uint64_t)S);
-      const int64_t ring = (int64_t)b * slots + offset[h];
-      const int64_t row = ((int64_t)b * (Hq / G) + h) * D;
+      const int64_t ring = ring_off[bh];
+      const int64_t row = (int64_t)bh * D;
       if (tid < D / 8) st16(kc + (ring + slot) * D + 8 * tid, ld16(kn + row + 8 * tid));
       if (tid < D)
         vc[(ring + (slot & ~31)) * D + tid * 32 + (slot & 31)] = vn[row + tid];
     }
   }
-  const int2 hc = head_chunks[h];
+  const int2 hc = head_chunks[bh];
   if (hc.y <= 1) return;
   const int dg = tid % DG;
   const int cg = tid / DG;
-  const int64_t part0 = (int64_t)b * n_chunks + hc.x;
+  const int64_t part0 = hc.x;
   float M = -INFINITY, L = 0.f;
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 8
@@ -384,24 +385,22 @@ template <int D, bool APPEND>
 hipError_t launch(const moa_plan& p, const void* q, const void* kc, const void* vc, void* o,
                   void* ws, const void* kn, const void* vn, int64_t pos, hipStream_t s) {
   const float scale_log2 = kLog2e / sqrtf((float)D);
-  const int64_t parts = (int64_t)p.B * p.n_chunks;
   DecodeWs w = decode_ws_layout(p, ws);
-  hipLaunchKernelGGL((decode_kernel<D, APPEND>), dim3((unsigned)parts), dim3(256), 0, s,
+  hipLaunchKernelGGL((decode_kernel<D, APPEND>), dim3((unsigned)p.n_chunks), dim3(256), 0, s,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(kc),
-                     static_cast<const bf16*>(vc), p.dev.decode_chunks, p.dev.head_chunks,
-                     p.dev.span, p.dev.offset, p.slots, (int)p.n_chunks, p.Hq, p.G,
-                     scale_log2, static_cast<bf16*>(o), w.o, w.ml, static_cast<const bf16*>(kn),
-                     static_cast<const bf16*>(vn), pos);
+                     static_cast<const bf16*>(vc), p.dev.decode_chunks, p.dev.span, p.dev.ring,
+                     p.dev.seq_len, (int)p.N, p.Hq, p.G, scale_log2, static_cast<bf16*>(o), w.o,
+                     w.ml, static_cast<const bf16*>(kn), static_cast<const bf16*>(vn), pos);
   hipError_t e = hipGetLastError();
   // the combine runs when some head is split, and always for a fused append
   // (it writes the new rows)
   if (e != hipSuccess || (!p.any_split && !APPEND)) return e;
   hipLaunchKernelGGL((decode_combine_kernel<D, APPEND>), dim3((unsigned)(p.B * p.Hq)), dim3(256),
-                     0, s, p.dev.head_chunks, (int)p.n_chunks, p.Hq, p.G, scale_log2, w.o, w.ml,
+                     0, s, p.dev.head_chunks, p.Hq, p.G, scale_log2, w.o, w.ml,
                      static_cast<bf16*>(o), static_cast<const bf16*>(kn),
                      static_cast<const bf16*>(vn), const_cast<bf16*>(static_cast<const bf16*>(kc)),
-                     const_cast<bf16*>(static_cast<const bf16*>(vc)), p.dev.span, p.dev.offset,
-                     p.slots, pos);
+                     const_cast<bf16*>(static_cast<const bf16*>(vc)), p.dev.span, p.dev.ring,
+                     p.dev.seq_len, (int)p.N, pos);
   return hipGetLastError();
 }
 

@@ -80,33 +80,55 @@ int dev_upload(T** dst, const std::vector<T>& src) {
 
 void free_device(moa_plan* p) {
   hipFree(p->dev.span);
-  hipFree(p->dev.offset);
+  hipFree(p->dev.ring);
+  hipFree(p->dev.seq_len);
   hipFree(p->dev.prefill_items);
   hipFree(p->dev.decode_chunks);
   hipFree(p->dev.head_chunks);
   p->dev = moa::PlanDevice{};
 }
 
-// Prefill work list, shared by every sequence of the batch: each
-// (h_q, 128-row query tile) with the range of 64-key tiles holding at least
-// one kept pair.  The union of the windows of rows i0..i1 is the contiguous
-// key range [max(0, i0 - S + 1), i1], so the live tiles form one range.
-// Sorted by tile count (longest first, so the tail of the launch holds the
-// short items), ties in (h_q, q_tile) order.  The launch runs item-major with
-// the sequence index fastest.
+// Span and ring tables of every (sequence, KV head): S = span_of(alpha_h,
+// beta_h, N_b); sequence b's rings follow each other (pitch: span rounded up
+// to 32 slots), and the sequences' blocks follow each other.
+void build_ring_tables(moa_plan* p, const int64_t* alpha, const double* beta) {
+  p->span.resize((size_t)p->B * p->Hkv);
+  p->ring.resize((size_t)p->B * p->Hkv);
+  int64_t total = 0;
+  for (int32_t b = 0; b < p->B; ++b)
+    for (int32_t h = 0; h < p->Hkv; ++h) {
+      const size_t i = (size_t)b * p->Hkv + h;
+      p->span[i] = (b > 0 && !p->ragged) ? p->span[h] : span_of(alpha[h], beta[h], p->seq_len[b]);
+      p->ring[i] = total;
+      total += ((int64_t)p->span[i] + 31) / 32 * 32;
+    }
+  p->total_slots = total;
+}
+
+// Prefill work list: each (h_q, 128-row query tile) of a sequence with the
+// range of 64-key tiles holding at least one kept pair.  The union of the
+// windows of rows i0..i1 is the contiguous key range [max(0, i0 - S + 1), i1],
+// so the live tiles form one range.  Sorted by tile count (longest first, so
+// the tail of the launch holds the short items), ties in (b, h_q, q_tile)
+// order.  Without per-sequence lengths one list serves every sequence (the
+// launch runs item-major, sequence index fastest); otherwise the list holds
+// the items of all sequences.
 void build_prefill_items(moa_plan* p) {
-  const int64_t n_qt = (p->N + moa::kPrefillBM - 1) / moa::kPrefillBM;
-  struct Item { int32_t h, qt, lo, hi; };
+  struct Item { int32_t bq, qt, lo, hi; };
   std::vector<Item> items;
-  items.reserve((size_t)p->Hq * n_qt);
-  for (int32_t h = 0; h < p->Hq; ++h) {
-    const int64_t s = p->span[h / p->G];
-    for (int64_t qt = 0; qt < n_qt; ++qt) {
-      const int64_t i0 = qt * moa::kPrefillBM;
-      const int64_t i1 = std::min<int64_t>(i0 + moa::kPrefillBM, p->N) - 1;
-      const int64_t j0 = std::max<int64_t>(0, i0 - s + 1);
-      items.push_back({h, (int32_t)qt, (int32_t)(j0 / moa::kPrefillBN),
-                       (int32_t)(i1 / moa::kPrefillBN)});
+  const int32_t nb = p->ragged ? p->B : 1;
+  for (int32_t b = 0; b < nb; ++b) {
+    const int64_t n = p->seq_len[b];
+    const int64_t n_qt = (n + moa::kPrefillBM - 1) / moa::kPrefillBM;
+    for (int32_t h = 0; h < p->Hq; ++h) {
+      const int64_t s = p->span[(size_t)b * p->Hkv + h / p->G];
+      for (int64_t qt = 0; qt < n_qt; ++qt) {
+        const int64_t i0 = qt * moa::kPrefillBM;
+        const int64_t i1 = std::min<int64_t>(i0 + moa::kPrefillBM, n) - 1;
+        const int64_t j0 = std::max<int64_t>(0, i0 - s + 1);
+        items.push_back({p->ragged ? b * p->Hq + h : h, (int32_t)qt,
+                         (int32_t)(j0 / moa::kPrefillBN), (int32_t)(i1 / moa::kPrefillBN)});
+      }
     }
   }
   std::stable_sort(items.begin(), items.end(), [](const Item& a, const Item& b) {
@@ -114,28 +136,30 @@ void build_prefill_items(moa_plan* p) {
   });
   p->prefill_items.resize(items.size() * 4);
   for (size_t i = 0; i < items.size(); ++i) {
-    p->prefill_items[4 * i + 0] = items[i].h;
+    p->prefill_items[4 * i + 0] = items[i].bq;
     p->prefill_items[4 * i + 1] = items[i].qt;
     p->prefill_items[4 * i + 2] = items[i].lo;
     p->prefill_items[4 * i + 3] = items[i].hi;
   }
+  p->prefill_bgrid = p->ragged ? 1 : p->B;
 }
 
-// Decode chunk list of one sequence: each head's S_h slots cut into chunks
-// of at most decode_chunk slots, heads in order.
+// Decode chunk list of all sequences: each ring's S slots cut into chunks of
+// at most decode_chunk slots, in (b, h) order.
 void build_decode_chunks(moa_plan* p) {
   const int32_t c = p->decode_chunk;
   p->decode_chunks.clear();
-  p->head_chunks.assign((size_t)p->Hkv * 2, 0);
-  int32_t idx = 0;
-  for (int32_t h = 0; h < p->Hkv; ++h) {
-    const int32_t s = p->span[h];
+  p->head_chunks.assign((size_t)p->B * p->Hkv * 2, 0);
+  p->any_split = false;
+  int64_t idx = 0;
+  for (int32_t bh = 0; bh < p->B * p->Hkv; ++bh) {
+    const int32_t s = p->span[bh];
     const int32_t cnt = (s + c - 1) / c;
     p->any_split |= cnt > 1;
-    p->head_chunks[2 * h + 0] = idx;
-    p->head_chunks[2 * h + 1] = cnt;
+    p->head_chunks[2 * (size_t)bh + 0] = (int32_t)idx;
+    p->head_chunks[2 * (size_t)bh + 1] = cnt;
     for (int32_t k = 0; k < cnt; ++k) {
-      p->decode_chunks.push_back(h);
+      p->decode_chunks.push_back(bh);
       p->decode_chunks.push_back(k * c);
       p->decode_chunks.push_back(std::min(c, s - k * c));
       p->decode_chunks.push_back(cnt);
@@ -199,6 +223,96 @@ int check_decode(moa_plan_t p, const void* q, const void* kc, const void* vc, in
   return set_device(p);
 }
 
+int create_plan(const moa_problem* pr, const int64_t* seq_len, uint32_t flags, moa_plan_t* out) {
+  if (!out) return fail(MOA_EINVAL, "out must not be NULL");
+  *out = nullptr;
+  if (!pr) return fail(MOA_EINVAL, "problem must not be NULL");
+  if (flags & ~MOA_PLAN_HOST_ONLY) return fail(MOA_EINVAL, "unknown flags 0x%x", flags);
+  if (pr->batch < 1) return fail(MOA_EINVAL, "batch must be >= 1 (got %d)", pr->batch);
+  if (pr->n_q_heads < 1) return fail(MOA_EINVAL, "n_q_heads must be >= 1 (got %d)", pr->n_q_heads);
+  int st = check_rules(pr->alpha, pr->beta, pr->n_kv_heads, pr->n_prompt);
+  if (st != MOA_OK) return st;
+  if (pr->n_q_heads % pr->n_kv_heads)
+    return fail(MOA_EINVAL, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)", pr->n_q_heads,
+                pr->n_kv_heads);
+  if (pr->n_q_heads / pr->n_kv_heads > 16)
+    return fail(MOA_EUNSUPPORTED, "query heads per KV head must be <= 16 (got %d)",
+                pr->n_q_heads / pr->n_kv_heads);
+  if (pr->head_dim != 64 && pr->head_dim != 128)
+    return fail(MOA_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", pr->head_dim);
+  if (pr->dtype != MOA_F32 && pr->dtype != MOA_BF16)
+    return fail(MOA_EUNSUPPORTED, "unknown dtype %d", pr->dtype);
+  if (seq_len) {
+    int64_t mx = 0;
+    for (int32_t b = 0; b < pr->batch; ++b) {
+      if (seq_len[b] < 1 || seq_len[b] > pr->n_prompt)
+        return fail(MOA_EINVAL, "seq_len[%d] = %lld must be in [1, n_prompt = %lld]", b,
+                    (long long)seq_len[b], (long long)pr->n_prompt);
+      mx = std::max(mx, seq_len[b]);
+    }
+    if (mx != pr->n_prompt)
+      return fail(MOA_EINVAL, "n_prompt (%lld) must equal the longest seq_len (%lld)",
+                  (long long)pr->n_prompt, (long long)mx);
+  }
+  // Every element index of the largest tensor must fit int64 comfortably and
+  // the per-launch item counts must fit int32 grids.
+  const double elems = (double)pr->batch * pr->n_q_heads * (double)pr->n_prompt * pr->head_dim;
+  if (elems > 9.0e15) return fail(MOA_EINVAL, "problem too large");
+  const double items = (double)pr->batch * pr->n_q_heads *
+                       ((pr->n_prompt + moa::kPrefillBM - 1) / moa::kPrefillBM);
+  if (items > 2.0e9) return fail(MOA_EINVAL, "too many prefill tiles for one launch");
+  if ((double)pr->batch * pr->n_kv_heads * (double)pr->n_prompt / 32.0 > 2.0e9)
+    return fail(MOA_EINVAL, "too many decode chunks for one launch");
+
+  moa_plan* p = new (std::nothrow) moa_plan;
+  if (!p) return fail(MOA_ENOMEM, "host allocation of the plan failed");
+  try {
+    p->B = pr->batch;
+    p->Hq = pr->n_q_heads;
+    p->Hkv = pr->n_kv_heads;
+    p->G = pr->n_q_heads / pr->n_kv_heads;
+    p->D = pr->head_dim;
+    p->N = pr->n_prompt;
+    p->dtype = pr->dtype;
+    p->ragged = seq_len != nullptr;
+    p->host_only = (flags & MOA_PLAN_HOST_ONLY) != 0;
+    p->seq_len.assign(p->B, p->N);
+    if (seq_len) std::copy(seq_len, seq_len + p->B, p->seq_len.begin());
+    build_ring_tables(p, pr->alpha, pr->beta);
+    build_prefill_items(p);
+    build_decode_chunks(p);
+  } catch (const std::bad_alloc&) {
+    delete p;
+    return fail(MOA_ENOMEM, "host allocation of plan tables failed");
+  }
+
+  if (!p->host_only) {
+    hipError_t e = hipGetDevice(&p->device);
+    if (e != hipSuccess) {
+      delete p;
+      return hip_fail(e, "hipGetDevice");
+    }
+    std::vector<int4> items(p->prefill_items.size() / 4), chunks(p->decode_chunks.size() / 4);
+    std::vector<int2> hc(p->head_chunks.size() / 2);
+    std::vector<int32_t> lens(p->seq_len.begin(), p->seq_len.end());
+    std::memcpy(items.data(), p->prefill_items.data(), p->prefill_items.size() * 4);
+    std::memcpy(chunks.data(), p->decode_chunks.data(), p->decode_chunks.size() * 4);
+    std::memcpy(hc.data(), p->head_chunks.data(), p->head_chunks.size() * 4);
+    if ((st = dev_upload(&p->dev.span, p->span)) != MOA_OK ||
+        (st = dev_upload(&p->dev.ring, p->ring)) != MOA_OK ||
+        (st = dev_upload(&p->dev.seq_len, lens)) != MOA_OK ||
+        (st = dev_upload(&p->dev.prefill_items, items)) != MOA_OK ||
+        (st = dev_upload(&p->dev.decode_chunks, chunks)) != MOA_OK ||
+        (st = dev_upload(&p->dev.head_chunks, hc)) != MOA_OK) {
+      free_device(p);
+      delete p;
+      return st;
+    }
+  }
+  *out = p;
+  return MOA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -227,83 +341,14 @@ int moa_ring_offsets(const int32_t* span, int32_t n_kv_heads, int64_t* offset,
 }
 
 int moa_plan_create(const moa_problem* pr, uint32_t flags, moa_plan_t* out) {
-  if (!out) return fail(MOA_EINVAL, "out must not be NULL");
-  *out = nullptr;
-  if (!pr) return fail(MOA_EINVAL, "problem must not be NULL");
-  if (flags & ~MOA_PLAN_HOST_ONLY) return fail(MOA_EINVAL, "unknown flags 0x%x", flags);
-  if (pr->batch < 1) return fail(MOA_EINVAL, "batch must be >= 1 (got %d)", pr->batch);
-  if (pr->n_q_heads < 1) return fail(MOA_EINVAL, "n_q_heads must be >= 1 (got %d)", pr->n_q_heads);
-  int st = check_rules(pr->alpha, pr->beta, pr->n_kv_heads, pr->n_prompt);
-  if (st != MOA_OK) return st;
-  if (pr->n_q_heads % pr->n_kv_heads)
-    return fail(MOA_EINVAL, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)", pr->n_q_heads,
-                pr->n_kv_heads);
-  if (pr->n_q_heads / pr->n_kv_heads > 16)
-    return fail(MOA_EUNSUPPORTED, "query heads per KV head must be <= 16 (got %d)",
-                pr->n_q_heads / pr->n_kv_heads);
-  if (pr->head_dim != 64 && pr->head_dim != 128)
-    return fail(MOA_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", pr->head_dim);
-  if (pr->dtype != MOA_F32 && pr->dtype != MOA_BF16)
-    return fail(MOA_EUNSUPPORTED, "unknown dtype %d", pr->dtype);
-  // Every element index of the largest tensor must fit int64 comfortably and
-  // the per-launch item counts must fit int32 grids.
-  const double elems = (double)pr->batch * pr->n_q_heads * (double)pr->n_prompt * pr->head_dim;
-  if (elems > 9.0e15) return fail(MOA_EINVAL, "problem too large");
-  const double items = (double)pr->batch * pr->n_q_heads *
-                       ((pr->n_prompt + moa::kPrefillBM - 1) / moa::kPrefillBM);
-  if (items > 2.0e9) return fail(MOA_EINVAL, "too many prefill tiles for one launch");
-  if ((double)pr->batch * pr->n_kv_heads * (double)pr->n_prompt / 32.0 > 2.0e9)
-    return fail(MOA_EINVAL, "too many decode chunks for one launch");
+  return create_plan(pr, nullptr, flags, out);
+}
 
-  moa_plan* p = new (std::nothrow) moa_plan;
-  if (!p) return fail(MOA_ENOMEM, "host allocation of the plan failed");
-  try {
-    p->B = pr->batch;
-    p->Hq = pr->n_q_heads;
-    p->Hkv = pr->n_kv_heads;
-    p->G = pr->n_q_heads / pr->n_kv_heads;
-    p->D = pr->head_dim;
-    p->N = pr->n_prompt;
-    p->dtype = pr->dtype;
-    p->host_only = (flags & MOA_PLAN_HOST_ONLY) != 0;
-    p->span.resize(p->Hkv);
-    p->offset.resize(p->Hkv);
-    for (int32_t h = 0; h < p->Hkv; ++h) p->span[h] = span_of(pr->alpha[h], pr->beta[h], p->N);
-    moa_ring_offsets(p->span.data(), p->Hkv, p->offset.data(), &p->slots);
-    build_prefill_items(p);
-    build_decode_chunks(p);
-    if ((double)p->B * (double)p->n_chunks > 2.0e9) {
-      delete p;
-      return fail(MOA_EINVAL, "too many decode chunks for one launch");
-    }
-  } catch (const std::bad_alloc&) {
-    delete p;
-    return fail(MOA_ENOMEM, "host allocation of plan tables failed");
-  }
-
-  if (!p->host_only) {
-    hipError_t e = hipGetDevice(&p->device);
-    if (e != hipSuccess) {
-      delete p;
-      return hip_fail(e, "hipGetDevice");
-    }
-    std::vector<int4> items(p->prefill_items.size() / 4), chunks(p->decode_chunks.size() / 4);
-    std::vector<int2> hc(p->Hkv);
-    std::memcpy(items.data(), p->prefill_items.data(), p->prefill_items.size() * 4);
-    std::memcpy(chunks.data(), p->decode_chunks.data(), p->decode_chunks.size() * 4);
-    std::memcpy(hc.data(), p->head_chunks.data(), p->head_chunks.size() * 4);
-    if ((st = dev_upload(&p->dev.span, p->span)) != MOA_OK ||
-        (st = dev_upload(&p->dev.offset, p->offset)) != MOA_OK ||
-        (st = dev_upload(&p->dev.prefill_items, items)) != MOA_OK ||
-        (st = dev_upload(&p->dev.decode_chunks, chunks)) != MOA_OK ||
-        (st = dev_upload(&p->dev.head_chunks, hc)) != MOA_OK) {
-      free_device(p);
-      delete p;
-      return st;
-    }
-  }
-  *out = p;
-  return MOA_OK;
+int moa_plan_create_ragged(const moa_problem* pr, const int64_t* seq_len, uint32_t flags,
+                           moa_plan_t* out) {
+  if (out) *out = nullptr;
+  if (!seq_len) return fail(MOA_EINVAL, "seq_len must not be NULL");
+  return create_plan(pr, seq_len, flags, out);
 }
 
 int moa_plan_destroy(moa_plan_t p) {
@@ -316,15 +361,27 @@ int moa_plan_destroy(moa_plan_t p) {
 int moa_plan_tables(moa_plan_t p, int32_t* span, int64_t* offset, int64_t* slots_per_seq) {
   int st = check_plan(p, false);
   if (st != MOA_OK) return st;
+  if (p->ragged)
+    return fail(MOA_EUNSUPPORTED, "plan has per-sequence lengths; use moa_plan_seq_tables");
+  // sequence 0's tables serve every sequence
+  if (span) std::copy(p->span.begin(), p->span.begin() + p->Hkv, span);
+  if (offset) std::copy(p->ring.begin(), p->ring.begin() + p->Hkv, offset);
+  if (slots_per_seq) *slots_per_seq = p->total_slots / p->B;
+  return MOA_OK;
+}
+
+int moa_plan_seq_tables(moa_plan_t p, int32_t* span, int64_t* ring_offset, int64_t* seq_len) {
+  int st = check_plan(p, false);
+  if (st != MOA_OK) return st;
   if (span) std::copy(p->span.begin(), p->span.end(), span);
-  if (offset) std::copy(p->offset.begin(), p->offset.end(), offset);
-  if (slots_per_seq) *slots_per_seq = p->slots;
+  if (ring_offset) std::copy(p->ring.begin(), p->ring.end(), ring_offset);
+  if (seq_len) std::copy(p->seq_len.begin(), p->seq_len.end(), seq_len);
   return MOA_OK;
 }
 
 int64_t moa_cache_elems(moa_plan_t p) {
   if (check_plan(p, false) != MOA_OK) return 0;
-  return (int64_t)p->B * p->slots * p->D;
+  return p->total_slots * p->D;
 }
 
 size_t moa_decode_workspace_bytes(moa_plan_t p) {
@@ -342,7 +399,7 @@ int64_t moa_max_batch(const moa_problem* pr, uint64_t budget_bytes) {
   // bytes(B) = both pools + the decode workspace moa_decode_workspace_bytes
   // reports for batch B; the largest B with bytes(B) <= budget
   const uint64_t elem = p->dtype == MOA_BF16 ? 2 : 4;
-  const uint64_t cache = 2ull * (uint64_t)p->slots * (uint64_t)p->D * elem;
+  const uint64_t cache = 2ull * (uint64_t)p->total_slots * (uint64_t)p->D * elem;
   const uint64_t ws = (uint64_t)p->n_chunks * (uint64_t)p->G * ((uint64_t)p->D + 2) * 4ull;
   moa_plan_destroy(p);
   auto bytes = [&](uint64_t b) {
@@ -358,8 +415,17 @@ int64_t moa_max_batch(const moa_problem* pr, uint64_t budget_bytes) {
 int64_t moa_plan_prefill_items(moa_plan_t p, int32_t* out) {
   int st = check_plan(p, false);
   if (st != MOA_OK) return st;
-  if (out) std::copy(p->prefill_items.begin(), p->prefill_items.end(), out);
-  return (int64_t)(p->prefill_items.size() / 4);
+  const size_t n = p->prefill_items.size() / 4;
+  if (out)
+    for (size_t i = 0; i < n; ++i) {
+      const int32_t bq = p->prefill_items[4 * i];
+      out[5 * i + 0] = p->ragged ? bq / p->Hq : -1;
+      out[5 * i + 1] = p->ragged ? bq % p->Hq : bq;
+      out[5 * i + 2] = p->prefill_items[4 * i + 1];
+      out[5 * i + 3] = p->prefill_items[4 * i + 2];
+      out[5 * i + 4] = p->prefill_items[4 * i + 3];
+    }
+  return (int64_t)n;
 }
 
 int64_t moa_plan_decode_chunks(moa_plan_t p, int32_t* out) {
@@ -368,9 +434,11 @@ int64_t moa_plan_decode_chunks(moa_plan_t p, int32_t* out) {
   const size_t n = p->decode_chunks.size() / 4;
   if (out)
     for (size_t i = 0; i < n; ++i) {
-      out[3 * i + 0] = p->decode_chunks[4 * i + 0];
-      out[3 * i + 1] = p->decode_chunks[4 * i + 1];
-      out[3 * i + 2] = p->decode_chunks[4 * i + 2];
+      const int32_t bh = p->decode_chunks[4 * i];
+      out[4 * i + 0] = bh / p->Hkv;
+      out[4 * i + 1] = bh % p->Hkv;
+      out[4 * i + 2] = p->decode_chunks[4 * i + 1];
+      out[4 * i + 3] = p->decode_chunks[4 * i + 2];
     }
   return (int64_t)n;
 }

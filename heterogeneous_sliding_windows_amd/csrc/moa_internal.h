@@ -18,29 +18,41 @@ constexpr int kPrefillBN = 64;
 constexpr int kDecodeChunk = 1024;
 
 struct PlanDevice {
-  int32_t* span = nullptr;          // [Hkv]
-  int64_t* offset = nullptr;        // [Hkv]
-  int4* prefill_items = nullptr;    // [n_prefill_items] {bh, q_tile, kt_lo, kt_hi}
-  int4* decode_chunks = nullptr;    // [n_chunks] {h_kv, first_slot, n_slots, chunks_of_head}
-  int2* head_chunks = nullptr;      // [Hkv] {first chunk index, chunk count}
+  int32_t* span = nullptr;          // [B*Hkv] span of ring (b, h)
+  int64_t* ring = nullptr;          // [B*Hkv] first slot of ring (b, h) in the pools
+  int32_t* seq_len = nullptr;       // [B] prompt length of each sequence
+  int4* prefill_items = nullptr;    // [n_prefill_items] {bq, q_tile, kt_lo, kt_hi}
+  int4* decode_chunks = nullptr;    // [n_chunks] {b*Hkv + h, first_slot, n_slots, chunks_of_ring}
+  int2* head_chunks = nullptr;      // [B*Hkv] {first chunk index, chunk count}
 };
 
 }  // namespace moa
 
+// A problem and its tables.  Sequence b's prompt has seq_len[b] <= N tokens;
+// in the [B, H, N, D] tensors it occupies the last seq_len[b] rows (left
+// padding), and its absolute position p sits at padded row p + N - seq_len[b].
+// A plan made without per-sequence lengths has seq_len[b] = N for every b.
 struct moa_plan {
   int32_t B = 0, Hq = 0, Hkv = 0, D = 0, G = 0, dtype = 0;
-  int64_t N = 0;
+  int64_t N = 0;                          // padded prompt length = max seq_len
+  bool ragged = false;                    // made by moa_plan_create_ragged
   bool host_only = false;
   int device = -1;
-  std::vector<int32_t> span;
-  std::vector<int64_t> offset;
-  int64_t slots = 0;                      // slots per sequence = sum of spans
-  std::vector<int32_t> prefill_items;     // 4 per item
-  std::vector<int32_t> decode_chunks;     // 4 per chunk (h, first, n, chunks_of_head)
-  std::vector<int32_t> head_chunks;       // 2 per KV head (first, count)
+  std::vector<int64_t> seq_len;           // [B]
+  std::vector<int32_t> span;              // [B*Hkv]
+  std::vector<int64_t> ring;              // [B*Hkv] first slot of each ring
+  int64_t total_slots = 0;                // slots of all sequences' rings
+  // Prefill items, 4 per item {bq, q_tile, kt_lo, kt_hi}.  Without per-
+  // sequence lengths every sequence shares the list: bq = h_q and the launch
+  // runs each item for all B sequences (prefill_bgrid = B).  Otherwise each
+  // item is one sequence's: bq = b*Hq + h_q, prefill_bgrid = 1.
+  std::vector<int32_t> prefill_items;
+  int32_t prefill_bgrid = 1;
+  std::vector<int32_t> decode_chunks;     // 4 per chunk, all sequences: {b*Hkv + h, first, n, chunks_of_ring}
+  std::vector<int32_t> head_chunks;       // 2 per (b, h): {first chunk, count}
   int32_t decode_chunk = moa::kDecodeChunk;
-  int64_t n_chunks = 0;                   // chunks per sequence
-  bool any_split = false;                 // some head has more than one chunk
+  int64_t n_chunks = 0;                   // decode chunks of all sequences
+  bool any_split = false;                 // some ring has more than one chunk
   moa::PlanDevice dev;
 };
 
@@ -61,25 +73,23 @@ hipError_t launch_append_decode_bf16(const moa_plan& p, const void* q, void* kc,
                                      const void* kn, const void* vn, int64_t pos, void* o,
                                      void* ws, hipStream_t s);
 
-// Workspace layout of the split-K decode: float o[n_parts][G][D], then
-// float2 ml[n_parts][G] (running max, sum), n_parts = B * n_chunks.
+// Workspace layout of the split-K decode: float o[n_chunks][G][D], then
+// float2 ml[n_chunks][G] (running max, sum), chunks of all sequences.
 struct DecodeWs {
   float* o;
   float2* ml;
 };
 
 inline size_t decode_ws_bytes(const moa_plan& p) {
-  const size_t parts = (size_t)p.B * (size_t)p.n_chunks;
-  size_t bytes = parts * (size_t)p.G * ((size_t)p.D + 2) * sizeof(float);
+  size_t bytes = (size_t)p.n_chunks * (size_t)p.G * ((size_t)p.D + 2) * sizeof(float);
   bytes = (bytes + 255) & ~(size_t)255;
   return bytes < 256 ? 256 : bytes;
 }
 
 inline DecodeWs decode_ws_layout(const moa_plan& p, void* ws) {
-  const size_t parts = (size_t)p.B * (size_t)p.n_chunks;
   DecodeWs w;
   w.o = static_cast<float*>(ws);
-  w.ml = reinterpret_cast<float2*>(w.o + parts * (size_t)p.G * (size_t)p.D);
+  w.ml = reinterpret_cast<float2*>(w.o + (size_t)p.n_chunks * (size_t)p.G * (size_t)p.D);
   return w;
 }
 

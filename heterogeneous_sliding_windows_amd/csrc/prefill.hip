@@ -8,9 +8,14 @@
 // of the causal matrix.
 //
 // Work items come from the plan: 128 query rows of one h_q and the range of
-// 64-key tiles that hold at least one kept pair, longest items first; the
-// grid runs every item for every sequence (sequence index fastest).
-// Tiles outside the window are never loaded.
+// 64-key tiles that hold at least one kept pair, longest items first; with
+// one prompt length the grid runs every item for every sequence (sequence
+// index fastest), with per-sequence lengths each item names its sequence.
+// Tiles outside the window are never loaded.  A sequence of N_b tokens
+// occupies the last N_b of the Npad rows of its [H, Npad, D] slices (left
+// padding): the kernels shift its base pointers by Npad - N_b rows and work
+// in its own positions 0 .. N_b - 1; padding rows are neither read nor
+// written.
 //
 // bf16 kernel (4 waves, 32 query rows each):
 //  * S^T = K Q^T on 32x32x16 bf16 MFMA, so each lane owns one query row and
@@ -53,8 +58,9 @@ template <int D, bool RING>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, const int4* __restrict__ items, const int32_t* __restrict__ span,
-    int B, int Hq, int Hkv, int G, int N, float scale_log2, bf16* __restrict__ kc,
-    bf16* __restrict__ vc, const int64_t* __restrict__ offset, int64_t slots) {
+    const int32_t* __restrict__ seq_len, int Bg, int Hq, int Hkv, int G, int Npad,
+    float scale_log2, bf16* __restrict__ kc, bf16* __restrict__ vc,
+    const int64_t* __restrict__ ring) {
   constexpr int KS = D / 16;       // k-steps of the Q.K product
   constexpr int OT = D / 32;       // 32-dim tiles of the output
   constexpr int KP = D + 8;        // K tile pitch (elements)
@@ -74,23 +80,28 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
   const int l32 = lane & 31;
   const int half = lane >> 5;
 
-  const int item = blockIdx.x / B;
-  const int b = blockIdx.x - item * B;   // sequence index runs fastest
+  // item and sequence: a shared item runs for Bg sequences (index fastest);
+  // a per-sequence item carries its sequence in it.x = b * Hq + h_q
+  const int item = blockIdx.x / Bg;
   const int4 it = items[item];
-  const int hq = it.x, qt = it.y, kt_lo = it.z, kt_hi = it.w;
+  const int b = it.x / Hq + (blockIdx.x - item * Bg);
+  const int hq = it.x % Hq, qt = it.y, kt_lo = it.z, kt_hi = it.w;
   const int bh = b * Hq + hq;
   const int hkv = hq / G;
-  const int S = span[hkv];
-  const bf16* qb = q + (int64_t)bh * N * D;
-  const bf16* kb = k + ((int64_t)b * Hkv + hkv) * N * D;
-  const bf16* vb = v + ((int64_t)b * Hkv + hkv) * N * D;
-  bf16* ob = o + (int64_t)bh * N * D;
+  const int S = span[b * Hkv + hkv];
+  // the sequence's own rows: the last N of the Npad padded rows
+  const int N = seq_len[b];
+  const int64_t pad = Npad - N;
+  const bf16* qb = q + ((int64_t)bh * Npad + pad) * D;
+  const bf16* kb = k + (((int64_t)b * Hkv + hkv) * Npad + pad) * D;
+  const bf16* vb = v + (((int64_t)b * Hkv + hkv) * Npad + pad) * D;
+  bf16* ob = o + ((int64_t)bh * Npad + pad) * D;
   // fused handoff: this workgroup's K/V rings (only g = 0 writes them)
   bf16* kring = nullptr;
   bf16* vring = nullptr;
   if constexpr (RING) {
     if (hq == hkv * G) {
-      const int64_t r0 = ((int64_t)b * slots + offset[hkv]) * D;
+      const int64_t r0 = ring[b * Hkv + hkv] * D;
       kring = kc + r0;
       vring = vc + r0;
     }
@@ -313,36 +324,39 @@ template <int D, bool RING>
 __global__ __launch_bounds__(256) void prefill_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ o, const int4* __restrict__ items, const int32_t* __restrict__ span,
-    int B, int Hq, int Hkv, int G, int N, float scale_log2, float* __restrict__ kc,
-    float* __restrict__ vc, const int64_t* __restrict__ offset, int64_t slots) {
+    const int32_t* __restrict__ seq_len, int Bg, int Hq, int Hkv, int G, int Npad,
+    float scale_log2, float* __restrict__ kc, float* __restrict__ vc,
+    const int64_t* __restrict__ ring) {
   constexpr int DH = D / 2;
   __shared__ __attribute__((aligned(16))) float Ks[BN * D];
   __shared__ __attribute__((aligned(16))) float Vs[BN * D];
   const int tid = threadIdx.x;
   const int half = tid & 1;
-  const int item = blockIdx.x / B;
-  const int b = blockIdx.x - item * B;
+  const int item = blockIdx.x / Bg;
   const int4 it = items[item];
-  const int hq = it.x, qt = it.y, kt_lo = it.z, kt_hi = it.w;
+  const int b = it.x / Hq + (blockIdx.x - item * Bg);
+  const int hq = it.x % Hq, qt = it.y, kt_lo = it.z, kt_hi = it.w;
   const int bh = b * Hq + hq;
   const int hkv = hq / G;
-  const int S = span[hkv];
-  const float* kb = k + ((int64_t)b * Hkv + hkv) * N * D;
-  const float* vb = v + ((int64_t)b * Hkv + hkv) * N * D;
+  const int S = span[b * Hkv + hkv];
+  const int N = seq_len[b];
+  const int64_t pad = Npad - N;
+  const float* kb = k + (((int64_t)b * Hkv + hkv) * Npad + pad) * D;
+  const float* vb = v + (((int64_t)b * Hkv + hkv) * Npad + pad) * D;
   const int my_q = qt * BM + (tid >> 1);
   // fused handoff (see the file comment): only g = 0 writes the rings
   float* kring = nullptr;
   float* vring = nullptr;
   if constexpr (RING) {
     if (hq == hkv * G) {
-      const int64_t r0 = ((int64_t)b * slots + offset[hkv]) * D;
+      const int64_t r0 = ring[b * Hkv + hkv] * D;
       kring = kc + r0;
       vring = vc + r0;
     }
   }
 
   float qr[DH];
-  const float* qrow = q + ((int64_t)bh * N + (my_q < N ? my_q : 0)) * D + half * DH;
+  const float* qrow = q + ((int64_t)bh * Npad + pad + (my_q < N ? my_q : 0)) * D + half * DH;
 #pragma unroll
   for (int e = 0; e < DH; e += 4) {
     const float4 x = *reinterpret_cast<const float4*>(qrow + e);
@@ -412,7 +426,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
   }
   if (my_q >= N) return;
   const float inv = 1.f / l_run;
-  float* orow = o + ((int64_t)bh * N + my_q) * D + half * DH;
+  float* orow = o + ((int64_t)bh * Npad + pad + my_q) * D + half * DH;
 #pragma unroll
   for (int e = 0; e < DH; e += 4)
     *reinterpret_cast<float4*>(orow + e) =
@@ -422,25 +436,25 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
 template <int D, bool RING>
 void launch_bf16(const moa_plan& p, const void* q, const void* k, const void* v, void* o, void* kc,
                  void* vc, hipStream_t s) {
-  const unsigned n_items = (unsigned)(p.prefill_items.size() / 4 * p.B);
+  const unsigned n_items = (unsigned)(p.prefill_items.size() / 4 * p.prefill_bgrid);
   const float scale_log2 = kLog2e / sqrtf((float)D);
   hipLaunchKernelGGL((prefill_bf16_kernel<D, RING>), dim3(n_items), dim3(256), 0, s,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                      static_cast<const bf16*>(v), static_cast<bf16*>(o), p.dev.prefill_items,
-                     p.dev.span, p.B, p.Hq, p.Hkv, p.G, (int)p.N, scale_log2,
-                     static_cast<bf16*>(kc), static_cast<bf16*>(vc), p.dev.offset, p.slots);
+                     p.dev.span, p.dev.seq_len, p.prefill_bgrid, p.Hq, p.Hkv, p.G, (int)p.N,
+                     scale_log2, static_cast<bf16*>(kc), static_cast<bf16*>(vc), p.dev.ring);
 }
 
 template <int D, bool RING>
 void launch_f32(const moa_plan& p, const void* q, const void* k, const void* v, void* o, void* kc,
                 void* vc, hipStream_t s) {
-  const unsigned n_items = (unsigned)(p.prefill_items.size() / 4 * p.B);
+  const unsigned n_items = (unsigned)(p.prefill_items.size() / 4 * p.prefill_bgrid);
   const float scale_log2 = kLog2e / sqrtf((float)D);
   hipLaunchKernelGGL((prefill_f32_kernel<D, RING>), dim3(n_items), dim3(256), 0, s,
                      static_cast<const float*>(q), static_cast<const float*>(k),
                      static_cast<const float*>(v), static_cast<float*>(o), p.dev.prefill_items,
-                     p.dev.span, p.B, p.Hq, p.Hkv, p.G, (int)p.N, scale_log2,
-                     static_cast<float*>(kc), static_cast<float*>(vc), p.dev.offset, p.slots);
+                     p.dev.span, p.dev.seq_len, p.prefill_bgrid, p.Hq, p.Hkv, p.G, (int)p.N,
+                     scale_log2, static_cast<float*>(kc), static_cast<float*>(vc), p.dev.ring);
 }
 
 }  // namespace

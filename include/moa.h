@@ -32,16 +32,26 @@
  *  - Threads: a plan is read-only after creation; distinct threads and
  *    streams may use one plan concurrently.  Calls that write the same cache
  *    or workspace must be ordered by the caller.
+ *  - Per-sequence prompt lengths (moa_plan_create_ragged): sequence b has a
+ *    prompt of N_b <= N tokens, N = the longest.  Every [.., N, D] tensor
+ *    keeps its shape; sequence b's prompt fills its last N_b rows (left
+ *    padding), so padded row r holds the sequence's own position
+ *    r - (N - N_b).  Spans are per sequence, S_{b,h} = the span rule at N_b,
+ *    and so are the rings.  Positions passed to the calls below are padded
+ *    positions: position P of the call is position P - (N - N_b) of sequence
+ *    b.  A plan without per-sequence lengths is the case N_b = N.
  *
  * KV cache ("ring pool") layout.  One pool for K and one for V, each of
- * B * slots_per_seq * D elements.  Head h owns a ring of S_h slots, stored
- * with a pitch of R_h = 32 * ceil(S_h / 32) slots (slots S_h .. R_h - 1 are
- * padding, never read as keys); offset[h] is the exclusive prefix sum of the
- * pitches and slots_per_seq their sum.  Absolute position p of head h lives
- * in slot p mod S_h.
- *    K element (b, h, slot, d) at  (b*slots_per_seq + offset[h] + slot)*D + d
- *    V element (b, h, slot, d) at  (b*slots_per_seq + offset[h])*D
- *                                  + (slot / 32)*32*D + d*32 + slot % 32
+ * moa_cache_elems() elements.  Ring (b, h) has S_{b,h} slots, stored with a
+ * pitch of R = 32 * ceil(S / 32) slots (slots S .. R - 1 are padding, never
+ * read as keys), starting at slot ring[b][h] of the pool: the rings of
+ * sequence b follow each other in head order, and the sequences' blocks
+ * follow each other (with one prompt length: ring[b][h] = b*slots_per_seq +
+ * offset[h], see moa_ring_offsets).  The sequence's own position p lives in
+ * slot p mod S_{b,h}.
+ *    K element (b, h, slot, d) at  (ring[b][h] + slot)*D + d
+ *    V element (b, h, slot, d) at  ring[b][h]*D + (slot / 32)*32*D + d*32
+ *                                  + slot % 32
  * (V rings are stored in blocks of 32 slots, each block dimension-major, so
  * decode's P.V product reads 8 consecutive slots of one dimension as a
  * matrix-core operand and streams each block as 8 KB of contiguous memory.)
@@ -119,16 +129,38 @@ int moa_ring_offsets(const int32_t* span, int32_t n_kv_heads, int64_t* offset,
  * G > 16, unknown dtype), MOA_ENOMEM, MOA_EHIP. */
 int moa_plan_create(const moa_problem* problem, uint32_t flags, moa_plan_t* out);
 
+/* Same, for a batch whose sequences have their own prompt lengths: seq_len
+ * is a host array of `batch` int64 entries in [1, n_prompt], read during the
+ * call, and problem->n_prompt must equal its largest entry (the padded
+ * length N).  Spans, rings and work lists are per sequence (see "Per-sequence
+ * prompt lengths" above): each input's own length sets its spans, as the
+ * rules scale with the input length (blog digest, section 2.1; the newx.sg
+ * paper page's "AI Summary" calls the sparsity sequence-length adaptive).
+ * Errors: those of moa_plan_create, and MOA_EINVAL for a null seq_len or a
+ * bad entry. */
+int moa_plan_create_ragged(const moa_problem* problem, const int64_t* seq_len,
+                           uint32_t flags, moa_plan_t* out);
+
 /* Free the plan's host and device tables.  NULL is accepted.  The caller must
  * ensure no enqueued work still reads the plan (synchronise first). */
 int moa_plan_destroy(moa_plan_t plan);
 
-/* Host copies of the plan's tables; any output pointer may be NULL.
- * span: int32[n_kv_heads]; offset: int64[n_kv_heads]. */
+/* Host copies of a plan's tables when every sequence shares them; any
+ * output pointer may be NULL.  span: int32[n_kv_heads]; offset:
+ * int64[n_kv_heads].  MOA_EUNSUPPORTED for a plan with per-sequence lengths
+ * (use moa_plan_seq_tables). */
 int moa_plan_tables(moa_plan_t plan, int32_t* span, int64_t* offset,
                     int64_t* slots_per_seq);
 
-/* Elements in ONE cache pool (K or V): B * slots_per_seq * D.  0 on error. */
+/* Host copies of the per-sequence tables of any plan; any output pointer may
+ * be NULL.  span: int32[B * n_kv_heads], S of ring (b, h) at b*Hkv + h;
+ * ring_offset: int64[B * n_kv_heads], first slot of ring (b, h) in the
+ * pools; seq_len: int64[B]. */
+int moa_plan_seq_tables(moa_plan_t plan, int32_t* span, int64_t* ring_offset,
+                        int64_t* seq_len);
+
+/* Elements in ONE cache pool (K or V): D times the slots of all rings.  0 on
+ * error. */
 int64_t moa_cache_elems(moa_plan_t plan);
 
 /* Bytes of device workspace moa_decode needs (>= 256).  0 on error. */
@@ -144,14 +176,15 @@ size_t moa_decode_workspace_bytes(moa_plan_t plan);
  * moa_plan_create). */
 int64_t moa_max_batch(const moa_problem* problem, uint64_t budget_bytes);
 
-/* Work-list inspection, for tests.  Prefill items are int32 quadruples
- * {h_q, q_tile, kt_lo, kt_hi}, shared by every sequence: query rows
- * q_tile*128 .. +127 read key tiles kt_lo .. kt_hi (64 keys each), i.e. every
- * tile holding at least one kept (query, key) pair and no other.  Items are
- * in launch order: cost (kt_hi - kt_lo + 1) descending, ties by (h_q,
- * q_tile) ascending; the launch runs each item for all B sequences in turn.
- * Decode chunks are int32 triples {h_kv, first_slot, n_slots} for one
- * sequence, in launch order; each head's ring is cut into chunks of at most
+/* Work-list inspection, for tests.  Prefill items are int32 quintuples
+ * {b, h_q, q_tile, kt_lo, kt_hi}: query rows q_tile*128 .. +127 of sequence
+ * b (its own positions) read key tiles kt_lo .. kt_hi (64 keys each), i.e.
+ * every tile holding at least one kept (query, key) pair and no other; b = -1
+ * marks an item of a plan without per-sequence lengths, which the launch
+ * runs for every sequence in turn.  Items are in launch order: cost
+ * (kt_hi - kt_lo + 1) descending, ties in list order (b, h_q, q_tile).
+ * Decode chunks are int32 quadruples {b, h_kv, first_slot, n_slots} of all
+ * sequences, in launch order; each ring is cut into chunks of at most
  * moa_plan_decode_chunk() slots.  Pass out = NULL to get the count; the
  * return value is the item count (>= 0) or a negative moa_status. */
 int64_t moa_plan_prefill_items(moa_plan_t plan, int32_t* out);
@@ -164,7 +197,9 @@ int32_t moa_plan_decode_chunk(moa_plan_t plan);
  *   q [B, Hq, N, D], k and v [B, Hkv, N, D] (inputs), o [B, Hq, N, D]
  *   (output), all in the plan's dtype.
  *   o[b,h,i,:] = sum_{j=max(0,i-S+1)}^{i} softmax_j(q_i . k_j / sqrt(D)) v_j,
- *   S = span of KV head h / G.
+ *   S = span of KV head h / G (of sequence b), i and j the sequence's own
+ *   positions; with per-sequence lengths the padding rows of q, k and v are
+ *   not read and those of o are not written.
  * Blog digest section 2.1 (sliding-window base mask) and project page
  * "Finding 2" (per-head span; the figure keeps a band of the causal matrix).
  * Key tiles outside a head's window are never read.  Errors: MOA_EINVAL for
@@ -175,7 +210,7 @@ int moa_prefill(moa_plan_t plan, const void* q, const void* k, const void* v,
 
 /* Prefill (as moa_prefill) fused with the handoff of the prompt to the KV
  * rings (as moa_kv_append(pos0 = 0, n_new = N)) in one launch: positions
- * N - S_h .. N - 1 of every (b, h) go to slot p mod S_h of k_cache/v_cache
+ * N_b - S .. N_b - 1 of every (b, h) go to slot p mod S of k_cache/v_cache
  * (the layout above), read once from k and v while the attention streams
  * them.  Project page, "Demo" step 03 (the exported rules feed a kernel
  * with a fixed-size, head-specific cache).  o and the ring contents equal
@@ -186,20 +221,24 @@ int moa_prefill_handoff(moa_plan_t plan, const void* q, const void* k, const voi
 
 /* Write positions pos0 .. pos0 + n_new - 1 of every (b, h) into the ring
  * pools.  k_new, v_new: [B, Hkv, n_new, D] in the plan's dtype; row t holds
- * position pos0 + t.  Only the last S_h of them are written for head h (the
- * earlier ones would be overwritten in the same call), each into slot
- * p mod S_h.  pos0 = 0, n_new = N hands a prompt's K/V over to the cache
- * after prefill; n_new = 1, pos0 = p appends one decode token.  Errors:
- * MOA_EINVAL for null pointers, pos0 < 0, n_new < 1 or a host-only plan. */
+ * padded position pos0 + t, i.e. position p = pos0 + t - (N - N_b) of
+ * sequence b (rows with p < 0 are padding and are skipped).  Only the last
+ * S of the rows with p >= 0 are written for ring (b, h) (the earlier ones
+ * would be overwritten in the same call), each into slot p mod S.
+ * pos0 = 0, n_new = N hands the prompts' K/V (the prefill layout) over to
+ * the cache after prefill; n_new = 1, pos0 = P appends one decode token.
+ * Errors: MOA_EINVAL for null pointers, pos0 < 0, n_new < 1 or a host-only
+ * plan. */
 int moa_kv_append(moa_plan_t plan, void* k_cache, void* v_cache,
                   const void* k_new, const void* v_new, int64_t pos0,
                   int64_t n_new, void* stream);
 
-/* Decode attention for the token at absolute position pos >= N, whose key
- * and value moa_kv_append must already have written (append, then attend).
- * The span stays the one computed from the prompt length N (the deployed
- * cache has a fixed size), so head h attends positions pos - S_h + 1 .. pos,
- * which are exactly the S_h slots of its ring.
+/* Decode attention for the token at padded position pos >= N (position
+ * p = pos - (N - N_b) of sequence b), whose key and value moa_kv_append must
+ * already have written (append, then attend).  The span stays the one
+ * computed from the prompt length (the deployed cache has a fixed size), so
+ * ring (b, h) attends positions p - S + 1 .. p, which are exactly its S
+ * slots.
  *   q [B, Hq, D] (input), o [B, Hq, D] (output), plan dtype MOA_BF16.
  * Split-K: each head's ring is cut into chunks of at most
  * moa_plan_decode_chunk() slots; a head with one chunk writes o directly,
@@ -214,15 +253,18 @@ int moa_decode(moa_plan_t plan, const void* q, const void* k_cache,
                const void* v_cache, int64_t pos, void* o, void* workspace,
                size_t ws_bytes, void* stream);
 
-/* One decode step in one launch: moa_kv_append(pos, n_new = 1) of k_new,
- * v_new [B, Hkv, D] fused into moa_decode(pos).  The decode chunk that holds
- * slot pos mod S_h of a head takes the new key and value from k_new/v_new
- * and writes them to the ring after it has read its slots, so the ring is
- * read once and no second launch is needed.  Project page, "Demo" step 03
- * and "Inference speed and memory efficiency" (fixed-size per-head cache,
- * append then attend).  o and the ring contents afterwards equal those of
- * the two separate calls.  Same arguments, workspace and errors as
- * moa_decode, plus MOA_EINVAL for null k_new/v_new or pos >= 2^62. */
+/* One decode step without the separate append launch: moa_kv_append(pos,
+ * n_new = 1) of k_new, v_new [B, Hkv, D] fused into moa_decode(pos).  The
+ * decode chunk holding slot p mod S of a ring ignores that slot and adds the
+ * new key and value from k_new/v_new instead; the merge kernel, which runs
+ * after every chunk has read its slots, writes them into the ring (it runs
+ * even when no ring is split).  Project page, "Demo" step 03 and "Inference
+ * speed and memory efficiency" (fixed-size per-head cache, append then
+ * attend).  The ring contents afterwards equal those of the two separate
+ * calls; o equals theirs up to rounding (the new key's weight is not rounded
+ * to bfloat16 for a matrix-core product).  Same arguments, workspace and
+ * errors as moa_decode, plus MOA_EINVAL for null k_new/v_new or
+ * pos >= 2^62. */
 int moa_append_decode(moa_plan_t plan, const void* q, void* k_cache, void* v_cache,
                       const void* k_new, const void* v_new, int64_t pos, void* o,
                       void* workspace, size_t ws_bytes, void* stream);

@@ -23,17 +23,17 @@ def ring_pitch(s):
 
 
 def ring_k(pool, plan, b, h):
-    """[S_h, D] view of K ring (b, h) in the layout include/moa.h documents."""
-    s, d = int(plan.spans[h]), plan.head_dim
-    base = (b * plan.slots_per_seq + int(plan.offsets[h])) * d
+    """[S, D] view of K ring (b, h) in the layout include/moa.h documents."""
+    s, d = int(plan.seq_spans[b, h]), plan.head_dim
+    base = int(plan.ring_offsets[b, h]) * d
     return pool[base:base + s * d].view(s, d)
 
 
 def ring_v(pool, plan, b, h):
-    """[S_h, D] copy of V ring (b, h): stored in 32-slot blocks, each [D][32]."""
-    s, d = int(plan.spans[h]), plan.head_dim
+    """[S, D] copy of V ring (b, h): stored in 32-slot blocks, each [D][32]."""
+    s, d = int(plan.seq_spans[b, h]), plan.head_dim
     r = ring_pitch(s)
-    base = (b * plan.slots_per_seq + int(plan.offsets[h])) * d
+    base = int(plan.ring_offsets[b, h]) * d
     blocks = pool[base:base + r * d].view(r // 32, d, 32)     # [block][dim][slot]
     return blocks.permute(0, 2, 1).reshape(r, d)[:s]
 

@@ -1,0 +1,195 @@
+"""Per-sequence prompt lengths (left-padded ragged batch) against the oracle.
+
+Sequence b of a ragged plan must behave exactly like a batch of one with
+N = N_b: its spans are the rule at N_b, its prefill rows, ring contents and
+decode outputs are those the oracle computes for that sequence alone.  The
+padding rows of q, k and v hold NaN, so any read of them would poison the
+outputs; o is pre-filled with a sentinel that padding rows must keep.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import f64, log, max_err, ring_k, ring_positions, ring_v
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+SENTINEL = 7.0
+_BITS = {torch.bfloat16: torch.int16, torch.float32: torch.int32}
+
+
+def _bits(t):
+    return t.contiguous().view(_BITS[t.dtype]).numpy()
+
+
+def _poison(t, lens):
+    """NaN in the left-padding rows of a [B, H, N, D] tensor."""
+    n = t.shape[2]
+    for b, nb in enumerate(lens):
+        t[b, :, :n - nb] = float("nan")
+    return t
+
+
+def _check_rings(plan, kc, vc, kp, vp, ks, vs, t_done):
+    """Ring (b, h) holds the oracle's slots for sequence b's own history."""
+    kc_h, vc_h = kc.cpu(), vc.cpu()
+    n = plan.n_prompt
+    for b, nb in enumerate(plan.seq_len):
+        nb = int(nb)
+        pad = n - nb
+        for h in range(plan.n_kv_heads):
+            s = int(plan.seq_spans[b, h])
+            hist_k, hist_v = kp[b, h, pad:], vp[b, h, pad:]
+            if t_done:
+                hist_k = torch.cat([hist_k, ks[:t_done, b, h]])
+                hist_v = torch.cat([hist_v, vs[:t_done, b, h]])
+            pos = np.arange(nb + t_done)
+            exp_k, held = oracle.ring_expected(_bits(hist_k), pos, s, nb - 1 + t_done)
+            exp_v, _ = oracle.ring_expected(_bits(hist_v), pos, s, nb - 1 + t_done)
+            assert (held == ring_positions(s, nb - 1 + t_done)).all()
+            assert np.array_equal(_bits(ring_k(kc_h, plan, b, h)), exp_k), (b, h)
+            assert np.array_equal(_bits(ring_v(vc_h, plan, b, h)), exp_v), (b, h)
+
+
+CASES = [
+    # Hq, Hkv, D, seq_len, alpha, beta, dtype
+    (4, 2, 128, [300, 1, 64, 299], [0, 100], [0.5, 0.0], "bf16"),
+    (8, 4, 64, [1000, 513, 777], [0, 64, 300, 0], [0.25, 0.0, 0.0, 1.0], "bf16"),
+    (16, 2, 128, [2500, 2499, 1024, 1025, 31], [0, 1500], [1.0, 0.0], "bf16"),
+    (4, 2, 64, [333, 100, 200], [0, 200], [0.5, 0.0], "f32"),
+    (2, 2, 128, [257, 130], [0, 64], [1.0, 0.0], "f32"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_ragged_prefill_and_handoff(moa, case):
+    hq, hkv, d, lens, alpha, beta, dt = CASES[case]
+    bsz, n = len(lens), max(lens)
+    log(f"ragged prefill case {case}: B{bsz} Hq{hq} Hkv{hkv} D{d} lens {lens} {dt}")
+    plan = moa.Plan(bsz, hq, hkv, d, n, alpha, beta, dtype=dt, seq_len=lens)
+    q, k, v = workloads.prefill_inputs(bsz, hq, hkv, n, d, dt, 9000 + case)
+    q, k, v = _poison(q, lens), _poison(k, lens), _poison(v, lens)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    o = torch.full_like(qd, SENTINEL)
+    plan.prefill(qd, kd, vd, o)
+    o2 = torch.full_like(qd, SENTINEL)
+    kc, vc = plan.new_cache()
+    plan.prefill_handoff(qd, kd, vd, o2, kc, vc)
+    kc2, vc2 = plan.new_cache()
+    plan.kv_append(kc2, vc2, kd, vd, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)
+    o_h = o.cpu()
+    worst = 0.0
+    for b, nb in enumerate(lens):
+        pad = n - nb
+        assert list(plan.seq_spans[b]) == list(oracle.spans(alpha, beta, nb))
+        want = oracle.prefill(f64(q[b:b + 1, :, pad:]), f64(k[b:b + 1, :, pad:]),
+                              f64(v[b:b + 1, :, pad:]), plan.seq_spans[b])
+        err = max_err(f64(o_h[b:b + 1, :, pad:]), want)
+        worst = max(worst, err)
+        assert err <= TOL[dt], (b, nb, err)
+        assert (o_h[b, :, :pad] == SENTINEL).all(), b
+    log(f"case {case} worst err {worst:.3e}")
+    _check_rings(plan, kc, vc, k, v, None, None, 0)
+    _check_rings(plan, kc2, vc2, k, v, None, None, 0)
+
+
+DECODE_CASES = [c for c in CASES if c[6] == "bf16"]
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("case", range(len(DECODE_CASES)))
+def test_ragged_decode(moa, case, fused):
+    hq, hkv, d, lens, alpha, beta, _ = DECODE_CASES[case]
+    bsz, n, t_steps = len(lens), max(lens), 3
+    log(f"ragged decode case {case} fused={fused}: B{bsz} lens {lens}")
+    plan = moa.Plan(bsz, hq, hkv, d, n, alpha, beta, seq_len=lens)
+    _, kp, vp = workloads.prefill_inputs(bsz, hq, hkv, n, d, "bf16", 9100 + case)
+    kp, vp = _poison(kp, lens), _poison(vp, lens)
+    qs, ks, vs = workloads.decode_step_inputs(bsz, hq, hkv, t_steps, d, "bf16", 9101 + case)
+    kc, vc = plan.new_cache()
+    ws = plan.new_workspace()
+    plan.kv_append(kc, vc, kp.cuda(), vp.cuda(), 0)
+    outs = []
+    for t in range(t_steps):
+        o = torch.empty(bsz, hq, d, dtype=torch.bfloat16, device="cuda")
+        if fused:
+            plan.append_decode(qs[t].cuda(), kc, vc, ks[t].cuda(), vs[t].cuda(), n + t, o, ws)
+        else:
+            plan.kv_append(kc, vc, ks[t].unsqueeze(2).cuda(), vs[t].unsqueeze(2).cuda(), n + t)
+            plan.decode(qs[t].cuda(), kc, vc, n + t, o, ws)
+        outs.append(o.cpu())
+    torch.cuda.synchronize()
+    _check_rings(plan, kc, vc, kp, vp, ks, vs, t_steps)
+    got = np.stack([f64(o) for o in outs])
+    worst = 0.0
+    for b, nb in enumerate(lens):
+        pad = n - nb
+        want = oracle.decode(f64(qs[:, b:b + 1]), [f64(kp[b:b + 1, h, pad:]) for h in range(hkv)],
+                             [f64(vp[b:b + 1, h, pad:]) for h in range(hkv)],
+                             f64(ks[:, b:b + 1]), f64(vs[:, b:b + 1]), plan.seq_spans[b], nb)
+        err = max_err(got[:, b:b + 1], want)
+        worst = max(worst, err)
+        assert err <= TOL["bf16"], (b, nb, err)
+    log(f"case {case} worst err {worst:.3e}")
+
+
+def test_ragged_full_size_sampled(moa):
+    """Vicuna-7B-shaped rules (32 heads, N up to 16384), 16 sequences of seeded lengths,
+    device-filled prompt K/V handed over by the fused prefill, then fused decode steps;
+    sampled (b, h) against the oracle."""
+    name = "c2_decode"
+    w = workloads.WORKLOADS[name]
+    alpha, beta = workloads.rules(name)
+    rng = np.random.Generator(np.random.PCG64(4242))
+    lens = [int(x) for x in rng.integers(1, w.n_prompt + 1, 15)] + [w.n_prompt]
+    bsz, n, d, hq, hkv = len(lens), w.n_prompt, w.head_dim, w.n_q_heads, w.n_kv_heads
+    plan = moa.Plan(bsz, hq, hkv, d, n, alpha, beta, seq_len=lens)
+    log(f"ragged full size: B{bsz} lens {lens}")
+    shape_q, shape_kv = (bsz, hq, n, d), (bsz, hkv, n, d)
+    q = workloads.device_normal_(torch.empty(shape_q, dtype=torch.bfloat16, device="cuda"), 91)
+    k = workloads.device_normal_(torch.empty(shape_kv, dtype=torch.bfloat16, device="cuda"), 92)
+    v = workloads.device_normal_(torch.empty(shape_kv, dtype=torch.bfloat16, device="cuda"), 93)
+    o = torch.empty_like(q)
+    kc, vc = plan.new_cache()
+    ws = plan.new_workspace()
+    plan.prefill_handoff(q, k, v, o, kc, vc)
+    t_steps = 2
+    qs, ks, vs = workloads.decode_step_inputs(bsz, hq, hkv, t_steps, d, "bf16", 94)
+    outs = []
+    for t in range(t_steps):
+        od = torch.empty(bsz, hq, d, dtype=torch.bfloat16, device="cuda")
+        plan.append_decode(qs[t].cuda(), kc, vc, ks[t].cuda(), vs[t].cuda(), n + t, od, ws)
+        outs.append(od.cpu())
+    torch.cuda.synchronize()
+    g = hq // hkv
+    pairs = [(int(rng.integers(bsz)), int(rng.integers(hkv))) for _ in range(12)]
+    pairs += [(bsz - 1, 0), (int(np.argmin(lens)), 1)]
+    worst = 0.0
+    for b, h in pairs:
+        nb, pad = lens[b], n - lens[b]
+        s = int(plan.seq_spans[b, h])
+        assert s == int(oracle.spans(alpha, beta, nb)[h])
+        kb, vb = f64(k[b, h, pad:]), f64(v[b, h, pad:])
+        # prefill rows: the sequence's first, last and window-edge rows
+        rows = sorted({0, nb - 1, min(nb - 1, s), max(0, nb - s - 1)})
+        for hh in range(h * g, (h + 1) * g):
+            want = oracle.prefill_rows(f64(q[b, hh, pad:][rows]), kb, vb, s, rows)
+            err = max_err(f64(o[b, hh, pad:][rows]), want)
+            worst = max(worst, err)
+            assert err <= TOL["bf16"], ("prefill", b, h, hh, err)
+        for t in range(t_steps):
+            hist_k = np.concatenate([kb[nb - s:], f64(ks[:t + 1, b, h])])
+            hist_v = np.concatenate([vb[nb - s:], f64(vs[:t + 1, b, h])])
+            pos = np.arange(nb - s, nb + t + 1)
+            want = oracle.decode_step(f64(qs[t, b, h * g:(h + 1) * g]), hist_k, hist_v, pos,
+                                      nb + t, s)
+            err = max_err(f64(outs[t][b, h * g:(h + 1) * g]), want)
+            worst = max(worst, err)
+            assert err <= TOL["bf16"], ("decode", b, h, t, err)
+    log(f"ragged full size worst sampled err {worst:.3e}")

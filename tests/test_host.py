@@ -86,13 +86,13 @@ def test_workload_plan_tables(moa, name):
     plan.close()
 
 
-def _check_prefill_items(plan, n, span_of_q):
-    """Each (bh, q_tile) once; [kt_lo, kt_hi] = exactly the live 64-key tiles; LPT order."""
-    items = plan.prefill_items()
+def _check_prefill_items(items, n, n_q_heads, span_of_q):
+    """Items {b, h_q, q_tile, kt_lo, kt_hi} of one sequence with n tokens: each (h_q, q_tile)
+    once; [kt_lo, kt_hi] = exactly the live 64-key tiles of the oracle's mask rows."""
     n_qt = (n + 127) // 128
-    assert len(items) == plan.n_q_heads * n_qt
+    assert len(items) == n_q_heads * n_qt
     seen = set()
-    for hq, qt, lo, hi in items:
+    for _, hq, qt, lo, hi in items:
         assert (hq, qt) not in seen
         seen.add((hq, qt))
         s = span_of_q(hq)
@@ -100,13 +100,16 @@ def _check_prefill_items(plan, n, span_of_q):
         # brute force: live tiles from the explicit mask rows
         m = oracle.band_mask(s, n)[rows]
         live = [kt for kt in range((n + 63) // 64) if m[:, kt * 64:(kt + 1) * 64].any()]
-        assert live == list(range(lo, hi + 1)), (bh, qt, lo, hi, live[:3], live[-3:])
-    cost = items[:, 3] - items[:, 2]
+        assert live == list(range(lo, hi + 1)), (hq, qt, lo, hi, live[:3], live[-3:])
+
+
+def _check_lpt_order(items):
+    """Launch order: cost descending, ties in list order (b, h_q, q_tile)."""
+    cost = items[:, 4] - items[:, 3]
     assert (np.diff(cost) <= 0).all()
     for i in range(1, len(items)):
         if cost[i] == cost[i - 1]:
-            assert (items[i, 0], items[i, 1]) > (items[i - 1, 0], items[i - 1, 1])
-    return items
+            assert tuple(items[i, :3]) > tuple(items[i - 1, :3])
 
 
 @pytest.mark.parametrize("n,alpha,beta,hq,hkv", [
@@ -119,7 +122,10 @@ def test_prefill_items_bruteforce(moa, n, alpha, beta, hq, hkv):
     plan = moa.Plan(2, hq, hkv, 128, n, alpha, beta, host_only=True)
     s = oracle.spans(alpha, beta, n)
     g = hq // hkv
-    _check_prefill_items(plan, n, lambda h: int(s[h // g]))
+    items = plan.prefill_items()
+    assert (items[:, 0] == -1).all()          # one list serves every sequence
+    _check_prefill_items(items, n, hq, lambda h: int(s[h // g]))
+    _check_lpt_order(items)
 
 
 def test_prefill_items_full_size_tables(moa):
@@ -136,7 +142,7 @@ def test_prefill_items_full_size_tables(moa):
         j = np.arange(n)
         rng = np.random.Generator(np.random.PCG64(3))
         for idx in rng.integers(0, len(items), 200):
-            hq, qt, lo, hi = items[idx]
+            _, hq, qt, lo, hi = items[idx]
             sp = int(s[hq // g])
             r0, r1 = qt * 128, min(qt * 128 + 128, n) - 1
             kept = np.zeros(n, dtype=bool)
@@ -155,18 +161,27 @@ def test_decode_chunks_cover_rings(moa, name):
     plan = moa.Plan(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, alpha, beta,
                     host_only=True)
     ch = plan.decode_chunks()
-    c = plan.decode_chunk
-    for h, s in enumerate(plan.spans):
-        mine = ch[ch[:, 0] == h]
-        assert len(mine) == -(-int(s) // c)
-        covered = np.zeros(int(s), dtype=int)
-        for _, first, cnt in mine:
-            assert 1 <= cnt <= c
-            covered[first:first + cnt] += 1
-        assert (covered == 1).all()
-    assert plan.workspace_bytes >= w.batch * len(ch) * (w.n_q_heads // w.n_kv_heads) * \
+    _check_chunks(plan, ch)
+    assert plan.workspace_bytes >= len(ch) * (w.n_q_heads // w.n_kv_heads) * \
         (w.head_dim + 2) * 4
     plan.close()
+
+
+def _check_chunks(plan, ch):
+    """Every slot of every ring (b, h) in exactly one chunk of at most decode_chunk slots,
+    chunks in (b, h) order."""
+    c = plan.decode_chunk
+    assert (np.diff(ch[:, 0] * plan.n_kv_heads + ch[:, 1]) >= 0).all()
+    for b in range(plan.batch):
+        for h in range(plan.n_kv_heads):
+            s = int(plan.seq_spans[b, h])
+            mine = ch[(ch[:, 0] == b) & (ch[:, 1] == h)]
+            assert len(mine) == -(-s // c)
+            covered = np.zeros(s, dtype=int)
+            for _, _, first, cnt in mine:
+                assert 1 <= cnt <= c
+                covered[first:first + cnt] += 1
+            assert (covered == 1).all()
 
 
 @pytest.mark.parametrize("name", ["c2_decode", "c3_decode", "c4_decode"])
@@ -280,3 +295,85 @@ def test_error_message_is_thread_local(moa):
     t.join()
     assert msgs == [""]
     assert moa.last_error() != ""
+
+
+# ---------------------------------------------------------------------------
+# per-sequence prompt lengths (left-padded ragged batch)
+# ---------------------------------------------------------------------------
+
+RAGGED = [
+    # Hq, Hkv, D, seq_len, alpha, beta
+    (4, 2, 128, [300, 1, 64, 299], [0, 100], [0.5, 0.0]),
+    (8, 4, 64, [1000, 513, 777], [0, 64, 300, 0], [0.25, 0.0, 0.0, 1.0]),
+    (16, 2, 128, [2500, 2499, 1024, 1025, 31], [0, 1500], [1.0, 0.0]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(RAGGED)))
+def test_ragged_plan_tables(moa, case):
+    hq, hkv, d, lens, alpha, beta = RAGGED[case]
+    n = max(lens)
+    plan = moa.Plan(len(lens), hq, hkv, d, n, alpha, beta, seq_len=lens, host_only=True)
+    assert plan.ragged and plan.spans is None
+    assert list(plan.seq_len) == lens
+    pitches = []
+    for b, nb in enumerate(lens):
+        assert list(plan.seq_spans[b]) == list(oracle.spans(alpha, beta, nb)), b
+        pitches += _pitch(plan.seq_spans[b])
+    # rings of sequence 0, then sequence 1, ...; each head's ring at the prefix sum of pitches
+    off, tot = oracle.ring_offsets(pitches)
+    assert list(plan.ring_offsets.reshape(-1)) == list(off)
+    assert plan.cache_elems == tot * d
+    with pytest.raises(moa.MoaError) as e:
+        moa._check(moa._lib.moa_plan_tables(plan._h, None, None, None))
+    assert e.value.status == moa.MOA_EUNSUPPORTED
+    plan.close()
+
+
+def test_uniform_plan_seq_tables(moa):
+    """Without per-sequence lengths, the per-sequence tables repeat sequence 0's."""
+    plan = moa.Plan(3, 8, 4, 128, 1000, [0, 64, 300, 0], [0.25, 0.0, 0.0, 1.0], host_only=True)
+    for b in range(3):
+        assert list(plan.seq_spans[b]) == list(plan.spans)
+        assert list(plan.ring_offsets[b]) == list(b * plan.slots_per_seq + plan.offsets)
+    assert list(plan.seq_len) == [1000] * 3
+    plan.close()
+
+
+@pytest.mark.parametrize("case", range(len(RAGGED)))
+def test_ragged_prefill_items_bruteforce(moa, case):
+    hq, hkv, d, lens, alpha, beta = RAGGED[case]
+    plan = moa.Plan(len(lens), hq, hkv, d, max(lens), alpha, beta, seq_len=lens, host_only=True)
+    items = plan.prefill_items()
+    g = hq // hkv
+    for b, nb in enumerate(lens):
+        s = oracle.spans(alpha, beta, nb)
+        _check_prefill_items(items[items[:, 0] == b], nb, hq, lambda h: int(s[h // g]))
+    assert set(items[:, 0]) == set(range(len(lens)))
+    _check_lpt_order(items)
+    plan.close()
+
+
+@pytest.mark.parametrize("case", range(len(RAGGED)))
+def test_ragged_decode_chunks(moa, case):
+    hq, hkv, d, lens, alpha, beta = RAGGED[case]
+    plan = moa.Plan(len(lens), hq, hkv, d, max(lens), alpha, beta, seq_len=lens, host_only=True)
+    _check_chunks(plan, plan.decode_chunks())
+    plan.close()
+
+
+def test_ragged_plan_errors(moa):
+    args = dict(batch=3, n_q_heads=4, n_kv_heads=2, head_dim=128, n_prompt=100,
+                alpha=[0, 0], beta=[0.5, 0.5], dtype="bf16", host_only=True)
+    for lens in ([100, 0, 5], [100, 101, 5], [99, 50, 5], [-1, 100, 3]):
+        with pytest.raises(moa.MoaError) as e:
+            moa.Plan(**args, seq_len=lens)
+        assert e.value.status == moa.MOA_EINVAL, lens
+    with pytest.raises(ValueError):
+        moa.Plan(**args, seq_len=[100, 50])
+    out = moa._P()
+    a, ap = moa._i64([0, 0])
+    b, bp = moa._f64([0.5, 0.5])
+    pr = moa._Problem(3, 4, 2, 128, 100, ap, bp, moa.MOA_BF16)
+    assert moa._lib.moa_plan_create_ragged(ctypes.byref(pr), None, moa.MOA_PLAN_HOST_ONLY,
+                                           ctypes.byref(out)) == moa.MOA_EINVAL
