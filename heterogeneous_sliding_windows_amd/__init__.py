@@ -331,3 +331,6 @@ class Plan:
 
     def __exit__(self, *exc):
         self.close()
+
+
+from . import rules  # noqa: E402,F401  (per-layer rules files; needs Plan above)

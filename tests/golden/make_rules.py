@@ -1,12 +1,14 @@
-"""Write tests/golden/rules.json: the seeded per-head (alpha, beta) rule sets.
+"""Write tests/golden/rules.json (the seeded per-head (alpha, beta) rule sets)
+and tests/golden/model_rules.json (a seeded rule set for every layer of a
+32-layer, 32-head model, in the per-layer rules file format).
 
 The rule sets are inputs of the synthetic workloads, drawn from the discrete
 candidate grids the workloads define and rejection-sampled to a target mean
 density (mean S_h / N).  Spans are computed by the oracle only; nothing here
 touches the HIP path.  Run from the repository root:
 
-    python tests/golden/make_rules.py            # rewrite rules.json
-    python tests/golden/make_rules.py --check    # verify the committed file
+    python tests/golden/make_rules.py            # rewrite both files
+    python tests/golden/make_rules.py --check    # verify the committed files
 
 Sampling procedure (a reading; the density target has no stated tolerance or
 draw order): with numpy's PCG64 seeded by `seed`, each attempt draws every
@@ -41,6 +43,9 @@ SPECS = {
 }
 TOL = 0.01
 MAX_ATTEMPTS = 2_000_000
+# per-layer file: layer l drawn like "c1" (50 % grid at N = 8192) with seed
+# MODEL_SEED + l
+MODEL_SEED, MODEL_LAYERS, MODEL_HEADS, MODEL_N, MODEL_TARGET = 1100, 32, 32, 8192, 0.50
 
 
 def draw(seed, heads, n, target, split):
@@ -74,22 +79,35 @@ def build():
     return {name: draw(*spec) for name, spec in SPECS.items()}
 
 
+def build_model():
+    """The per-layer rules document ({"format": "moa-rules", "version": 1, ...})."""
+    layers = []
+    for layer in range(MODEL_LAYERS):
+        r = draw(MODEL_SEED + layer, MODEL_HEADS, MODEL_N, MODEL_TARGET, False)
+        layers.append({"alpha": r["alpha"], "beta": r["beta"]})
+    return {"format": "moa-rules", "version": 1, "n_kv_heads": MODEL_HEADS, "layers": layers}
+
+
 def main():
-    path = os.path.join(HERE, "rules.json")
-    rules = build()
+    outputs = {"rules.json": build(), "model_rules.json": build_model()}
     if "--check" in sys.argv:
-        with open(path) as f:
-            stored = json.load(f)
-        if stored != rules:
-            print("rules.json differs from a fresh draw")
-            sys.exit(1)
-        print("rules.json matches")
-        return
-    with open(path, "w") as f:
-        json.dump(rules, f, indent=1)
-        f.write("\n")
-    for name, r in rules.items():
+        bad = False
+        for name, doc in outputs.items():
+            with open(os.path.join(HERE, name)) as f:
+                stored = json.load(f)
+            if stored != doc:
+                print(f"{name} differs from a fresh draw")
+                bad = True
+            else:
+                print(f"{name} matches")
+        sys.exit(1 if bad else 0)
+    for name, doc in outputs.items():
+        with open(os.path.join(HERE, name), "w") as f:
+            json.dump(doc, f, indent=1)
+            f.write("\n")
+    for name, r in outputs["rules.json"].items():
         print(name, "attempts", r["attempts"], "density", round(r["density"], 4))
+    print("model_rules.json:", MODEL_LAYERS, "layers")
 
 
 if __name__ == "__main__":

@@ -1,0 +1,68 @@
+"""A model's layers with their own rules (from the per-layer rules file) on the GPU.
+
+Each layer gets its own plan, rings and work lists; every layer's prefill,
+prompt handoff and decode steps must match the oracle run with that layer's
+spans, sequence by sequence.
+"""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import f64, log, max_err
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def test_layers_from_rules_file(moa):
+    import heterogeneous_sliding_windows_amd.rules as rules
+    full = rules.load(os.path.join(GOLDEN, "model_rules.json"))
+    # the first 3 layers, first 8 KV heads of each (GQA, 2 query heads per KV head)
+    rs = rules.RuleSet([(a[:8], b[:8]) for a, b in full.layers[:3]])
+    lens = [1200, 700]
+    bsz, hq, hkv, d, n, t_steps = 2, 16, 8, 64, max(lens), 2
+    plans = rs.plans(bsz, hq, d, n, seq_len=lens)
+    assert len({tuple(p.seq_spans[0]) for p in plans}) == 3   # the layers' spans differ
+    worst = 0.0
+    try:
+        for layer, plan in enumerate(plans):
+            log(f"layer {layer}: spans {list(plan.seq_spans[0])} / {list(plan.seq_spans[1])}")
+            q, k, v = workloads.prefill_inputs(bsz, hq, hkv, n, d, "bf16", 9500 + layer)
+            qs, ks, vs = workloads.decode_step_inputs(bsz, hq, hkv, t_steps, d, "bf16",
+                                                      9600 + layer)
+            qd = q.cuda()
+            o = torch.empty_like(qd)
+            kc, vc = plan.new_cache()
+            ws = plan.new_workspace()
+            plan.prefill_handoff(qd, k.cuda(), v.cuda(), o, kc, vc)
+            outs = []
+            for t in range(t_steps):
+                od = torch.empty(bsz, hq, d, dtype=torch.bfloat16, device="cuda")
+                plan.append_decode(qs[t].cuda(), kc, vc, ks[t].cuda(), vs[t].cuda(), n + t, od, ws)
+                outs.append(od.cpu())
+            torch.cuda.synchronize()
+            got_d = np.stack([f64(x) for x in outs])
+            for b, nb in enumerate(lens):
+                pad = n - nb
+                spans = rs.spans(nb)[layer]
+                assert list(plan.seq_spans[b]) == list(spans)
+                want = oracle.prefill(f64(q[b:b + 1, :, pad:]), f64(k[b:b + 1, :, pad:]),
+                                      f64(v[b:b + 1, :, pad:]), spans)
+                err_p = max_err(f64(o[b:b + 1, :, pad:]), want)
+                want = oracle.decode(f64(qs[:, b:b + 1]),
+                                     [f64(k[b:b + 1, h, pad:]) for h in range(hkv)],
+                                     [f64(v[b:b + 1, h, pad:]) for h in range(hkv)],
+                                     f64(ks[:, b:b + 1]), f64(vs[:, b:b + 1]), spans, nb)
+                err_d = max_err(got_d[:, b:b + 1], want)
+                worst = max(worst, err_p, err_d)
+                assert err_p <= 2e-2 and err_d <= 2e-2, (layer, b, err_p, err_d)
+    finally:
+        for p in plans:
+            p.close()
+    log(f"layers: worst err {worst:.3e}")
