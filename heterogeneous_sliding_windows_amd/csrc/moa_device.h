@@ -10,12 +10,15 @@ namespace moa {
 typedef __bf16 bf16;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 
 constexpr float kLog2e = 1.4426950408889634f;
+// (1, 1) in bf16: the second operand of a two-element bf16 sum by dot product
+__device__ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
   u32x4 z = {0u, 0u, 0u, 0u};

@@ -11,7 +11,10 @@
 // 64-key tiles that hold at least one kept pair, longest items first; with
 // one prompt length the grid runs every item for every sequence (sequence
 // index fastest), with per-sequence lengths each item names its sequence.
-// Tiles outside the window are never loaded.  A sequence of N_b tokens
+// Tiles outside the window are never loaded.  The launch order is
+// XCD-aware: each of the 8 XCDs runs runs of 16 consecutive work units, so
+// neighbouring query tiles of a head (overlapping key windows) meet in the
+// same L2 instead of being spread over all eight.  A sequence of N_b tokens
 // occupies the last N_b of the Npad rows of its [H, Npad, D] slices (left
 // padding): the kernels shift its base pointers by Npad - N_b rows and work
 // in its own positions 0 .. N_b - 1; padding rows are neither read nor
@@ -60,7 +63,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
     bf16* __restrict__ o, const int4* __restrict__ items, const int32_t* __restrict__ span,
     const int32_t* __restrict__ seq_len, int Bg, int Hq, int Hkv, int G, int Npad,
     float scale_log2, bf16* __restrict__ kc, bf16* __restrict__ vc,
-    const int64_t* __restrict__ ring) {
+    const int64_t* __restrict__ ring, int n_wg) {
   constexpr int KS = D / 16;       // k-steps of the Q.K product
   constexpr int OT = D / 32;       // 32-dim tiles of the output
   constexpr int KP = D + 8;        // K tile pitch (elements)
@@ -82,9 +85,21 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
 
   // item and sequence: a shared item runs for Bg sequences (index fastest);
   // a per-sequence item carries its sequence in it.x = b * Hq + h_q
-  const int item = blockIdx.x / Bg;
+  // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin, so the
+  // k-th workgroup of XCD x takes work unit (k / C) * 8C + x * C + k % C:
+  // each XCD runs C consecutive units (neighbouring query tiles of one head,
+  // whose key windows overlap) together and they share its L2.  The grid is
+  // padded to a multiple of 8C; the padding workgroups exit here.
+  int lin = blockIdx.x;
+  {
+    constexpr int C = kPrefillXcdChunk;
+    const int x = lin & 7, k = lin >> 3;
+    lin = ((k / C) * 8 + x) * C + (k % C);
+    if (lin >= n_wg) return;
+  }
+  const int item = lin / Bg;
   const int4 it = items[item];
-  const int b = it.x / Hq + (blockIdx.x - item * Bg);
+  const int b = it.x / Hq + (lin - item * Bg);
   const int hq = it.x % Hq, qt = it.y, kt_lo = it.z, kt_hi = it.w;
   const int bh = b * Hq + hq;
   const int hkv = hq / G;
@@ -110,17 +125,31 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
   const int iw0 = qt * BM + wave * 32;  // first query row of this wave
   const int my_q = iw0 + l32;
 
+  // Q pre-scaled by log2(e)/sqrt(D): the scores come out in the exp2 domain
   bf16x8 qop[KS];
 #pragma unroll
-  for (int s = 0; s < KS; ++s)
-    qop[s] = my_q < N ? ld16(qb + (int64_t)my_q * D + 16 * s + 8 * half) : zero_bf16x8();
+  for (int s = 0; s < KS; ++s) {
+    const bf16x8 x = my_q < N ? ld16(qb + (int64_t)my_q * D + 16 * s + 8 * half) : zero_bf16x8();
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = (float)x[e] * scale_log2;
+    qop[s] = to_bf16x8(f);
+  }
 
   floatx16 acc[OT];
 #pragma unroll
   for (int t = 0; t < OT; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  // m_run: the row's running max (exp2 domain), -inf before its first kept
+  // key.  m_ref: the reference the scores are taken against (m_run once set,
+  // 0 before); -m_ref seeds the Q.K accumulators, so the matrix cores return
+  // score - m_ref, the exp2 argument itself.
+  float m_run = -INFINITY, m_ref = 0.f;
+  float l_a = 0.f, l_b = 0.f;   // row sum, two partial chains
+  floatx16 minit;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) minit[r] = 0.f;
 
   // staging registers for one K/V tile
   bf16x8 kst[KPASS];
@@ -233,8 +262,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
       floatx16 st[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st[t][r] = 0.f;
+        st[t] = minit;
         const bf16* krow = &Ks[buf][(32 * t + kperm) * KP + 8 * half];
 #pragma unroll
         for (int s = 0; s < KS; ++s) st[t] = mfma32(ld16(krow + 16 * s), qop[s], st[t]);
@@ -247,7 +275,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      // st[t][r] is the score of query my_q and key j0 + 32t + 16(r>>3) + 8half + (r&7)
+      // st[t][r] is score - m_ref of query my_q and key
+      // j0 + 32t + 16(r>>3) + 8half + (r&7)
       if (!full) {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -264,31 +293,43 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[t][r]);
       mx = wave_max_xor(mx, 32);
-      // Lazy rescale: the reference max m_run moves (and O, l are rescaled)
-      // only when some row's tile max exceeds it by more than 2^8 in the exp2
-      // domain; otherwise p <= 256, harmless in fp32 and bf16.  The final
-      // O / l is unchanged.  (m_run = -inf compares as +inf growth.)
-      if (__ballot((mx - m_run) * scale_log2 > 8.f)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;  // row with no kept key yet
-        const float alpha = fast_exp2((m_run - m_use) * scale_log2);
-        m_run = m_new;
-        l_run *= alpha;
+      // Lazy rescale: the reference moves (and O, l are rescaled) only when
+      // some row's tile max exceeds it by more than 8 in the exp2 domain, or
+      // sets it at the row's first kept key; otherwise p <= 256, harmless in
+      // fp32 and bf16.  The final O / l is unchanged.
+      if (__ballot(mx > 8.f || (m_run == -INFINITY && mx != -INFINITY))) {
+        const float m_new = fmaxf(m_run, mx == -INFINITY ? -INFINITY : m_ref + mx);
+        const bool set = m_new != -INFINITY;   // else: no kept key yet, nothing moves
+        const float alpha = set ? fast_exp2(m_run - m_new) : 1.f;   // 0 at the first key
+        const float delta = set ? m_new - m_ref : 0.f;
+        if (set) {
+          m_run = m_new;
+          m_ref = m_new;
+        }
+        l_a *= alpha;
+        l_b *= alpha;
 #pragma unroll
         for (int t = 0; t < OT; ++t) acc[t] *= alpha;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) st[t] -= delta;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) minit[r] = -m_ref;
       }
-      const float mb = (m_run == -INFINITY ? 0.f : m_run) * scale_log2;
       float p[2][16];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          p[t][r] = fast_exp2(__builtin_fmaf(st[t][r], scale_log2, -mb));
-          l_run += p[t][r];
-        }
+        for (int r = 0; r < 16; ++r) p[t][r] = fast_exp2(st[t][r]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const bf16x8 pop = to_bf16x8(&p[j >> 1][8 * (j & 1)]);
+        // the row sum of the bf16 weights the P.V product uses, two per step
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bf16x2 pair = {pop[2 * i], pop[2 * i + 1]};
+          if (i & 1) l_b = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, l_b, false);
+          else       l_a = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, l_a, false);
+        }
         const bf16* vrow = &Vt[buf][l32 * VP + 16 * j + 8 * half];
 #pragma unroll
         for (int t = 0; t < OT; ++t) acc[t] = mfma32(ld16(vrow + 32 * t * VP), pop, acc[t]);
@@ -305,6 +346,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
     __syncthreads();
   }
 
+  float l_run = l_a + l_b;
   l_run += __shfl_xor(l_run, 32, 64);
   if (my_q >= N) return;
   const float inv = 1.f / l_run;
@@ -438,11 +480,14 @@ void launch_bf16(const moa_plan& p, const void* q, const void* k, const void* v,
                  void* vc, hipStream_t s) {
   const unsigned n_items = (unsigned)(p.prefill_items.size() / 4 * p.prefill_bgrid);
   const float scale_log2 = kLog2e / sqrtf((float)D);
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, RING>), dim3(n_items), dim3(256), 0, s,
+  constexpr unsigned round = 8 * kPrefillXcdChunk;
+  const unsigned grid = (n_items + round - 1) / round * round;
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, RING>), dim3(grid), dim3(256), 0, s,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                      static_cast<const bf16*>(v), static_cast<bf16*>(o), p.dev.prefill_items,
                      p.dev.span, p.dev.seq_len, p.prefill_bgrid, p.Hq, p.Hkv, p.G, (int)p.N,
-                     scale_log2, static_cast<bf16*>(kc), static_cast<bf16*>(vc), p.dev.ring);
+                     scale_log2, static_cast<bf16*>(kc), static_cast<bf16*>(vc), p.dev.ring,
+                     (int)n_items);
 }
 
 template <int D, bool RING>
