@@ -77,4 +77,29 @@ __device__ __forceinline__ float wave_max_xor(float x, int mask) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+
+// LDS-direct buffer load: lane l's 16 bytes at voff + soff of the resource
+// land at LDS byte (lds + 16 l) (one wave fills 1 KB).  Out-of-range reads
+// give zeros.  Not tracked by the compiler's wait counting: the caller waits
+// with vmcnt(0) before the data is read.  The s_nop is the one wait state a
+// write of M0 needs before an LDS-direct load reads it.
+__device__ __forceinline__ void lds_direct_ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                uint32_t soff, void* lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(r), "s"(soff), "{m0}"(m0)
+               : "memory");
+}
+
+// Transposed LDS read (ds_read_b64_tr_b16) at an 8-byte aligned LDS address.
+// Within each 16-lane group, lane i names 4 consecutive 16-bit elements of
+// row i/4 of a 4 x 16 block (columns 4*(i%4) .. +3); lane j receives column
+// j of the block's 4 rows.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const void* p) {
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                        (__attribute__((address_space(3))) s16x4*)(p)));
+}
+
 }  // namespace moa

@@ -27,10 +27,13 @@
 //    reads key 16a + 8h + 4b + c), which puts the scores of lane half h on
 //    keys 16j + 8h .. +7 of P.V step j: the P^T operand is the lane's own
 //    scores, converted to bf16, with no data movement;
-//  * K tiles are staged in LDS row-major, V tiles transposed (V^T rows are
-//    the P.V A operand: 8 consecutive keys of one dimension per lane);
-//  * LDS tiles are double-buffered: tile t+1 is stored and tile t+2's
-//    global loads are issued before tile t is computed (one barrier a tile);
+//  * K and V tiles go from memory straight into LDS (16-byte LDS-direct
+//    buffer loads, no staging registers), in a chunk-swizzled layout that
+//    both fragment reads meet without bank conflicts; the V^T operand of the
+//    P.V product (8 consecutive keys of one dimension per lane) comes from
+//    two transposed LDS reads (ds_read_b64_tr_b16);
+//  * LDS tiles are double-buffered: tile t+1's loads are issued before tile
+//    t is computed (one wait and one barrier a tile);
 //  * masks are evaluated only on tiles a wave's rows do not fully keep, and a
 //    wave skips tiles none of its rows keep;
 //  * online softmax in fp32 with exp2 and the 1/sqrt(D)*log2(e) scale folded;
@@ -45,8 +48,8 @@
 // whole prompt would.  Key tile kt is the diagonal tile of query tile
 // kt*BN/BM, whose item always streams it; the workgroup of the first query
 // head of each KV group (g = 0) stores the rows of its diagonal tiles that the
-// ring keeps, from the staging registers, while staging them to LDS.  Every
-// ring row is therefore written once, and K/V are read from HBM once.
+// ring keeps, reading them from LDS.  Every ring row is therefore written
+// once, and K/V are read from HBM once.
 
 #include "moa_device.h"
 #include "moa_internal.h"
@@ -57,6 +60,17 @@ namespace {
 constexpr int BM = kPrefillBM;
 constexpr int BN = kPrefillBN;
 
+// LDS layout of a 64-row K or V tile (row = key): 16-byte chunks (8 dims)
+// in groups of four; group cg holds its 64-byte slice of all 64 rows, and
+// the chunk's place inside the slice is XOR-swizzled by row bits 2-3.  Byte
+// offset of chunk c of row r:
+__device__ __forceinline__ constexpr int tile_off(int r, int c) {
+  return (c >> 2) * 4096 + r * 64 + (((c & 3) ^ ((r >> 2) & 3)) << 4);
+}
+// (One wave's 16-byte LDS-direct load fills 1 KB: 16 rows of one group.
+// The 16 lanes of an LDS read phase meet 16 different rows of one chunk
+// column in different banks, for the K reads and the transposed V reads.)
+
 template <int D, bool RING>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -66,16 +80,11 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
     const int64_t* __restrict__ ring, int n_wg) {
   constexpr int KS = D / 16;       // k-steps of the Q.K product
   constexpr int OT = D / 32;       // 32-dim tiles of the output
-  constexpr int KP = D + 8;        // K tile pitch (elements)
-  constexpr int VP = BN + 8;       // V^T tile pitch
-  constexpr int CPR = D / 8;       // 16-byte chunks per K row
-  constexpr int RPP = 256 / CPR;   // K rows per load pass
-  constexpr int KPASS = BN / RPP;
-  constexpr int NKG = 256 / CPR;   // V key groups
-  constexpr int KPT = BN / NKG;    // keys per thread in the V transpose
-  static_assert(KPT == 2 || KPT == 4, "V transpose");
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][BN * KP];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[2][D * VP];
+  constexpr int ROWB = D * 2;      // bytes of a K/V row
+  constexpr int TILEB = BN * ROWB; // bytes of a K or V tile
+  constexpr int NDMA = D / 32;     // LDS-direct rounds per tile (chunk groups)
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2][BN * D];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2][BN * D];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -83,8 +92,6 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
   const int l32 = lane & 31;
   const int half = lane >> 5;
 
-  // item and sequence: a shared item runs for Bg sequences (index fastest);
-  // a per-sequence item carries its sequence in it.x = b * Hq + h_q
   // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin, so the
   // k-th workgroup of XCD x takes work unit (k / C) * 8C + x * C + k % C:
   // each XCD runs C consecutive units (neighbouring query tiles of one head,
@@ -93,8 +100,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
   int lin = blockIdx.x;
   {
     constexpr int C = kPrefillXcdChunk;
-    const int x = lin & 7, k = lin >> 3;
-    lin = ((k / C) * 8 + x) * C + (k % C);
+    const int x = lin & 7, kk = lin >> 3;
+    lin = ((kk / C) * 8 + x) * C + (kk % C);
     if (lin >= n_wg) return;
   }
   const int item = lin / Bg;
@@ -151,121 +158,117 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
 #pragma unroll
   for (int r = 0; r < 16; ++r) minit[r] = 0.f;
 
-  // staging registers for one K/V tile
-  bf16x8 kst[KPASS];
-  bf16x8 vst[KPT];
-  const int kchunk = tid % CPR;
-  const int krow0 = tid / CPR;
-  const int vdg = tid / NKG;  // 8-dim group of the V transpose
-  const int vkg = tid % NKG;  // key group of the V transpose
-
-  // K and V of this (b, h_kv) as buffer resources: rows at or past N read as
-  // zero, so the staging loads need no per-row predicate.
-  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(kb, (uint32_t)N * D * 2);
-  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(vb, (uint32_t)N * D * 2);
-  const uint32_t koff = (uint32_t)krow0 * D * 2 + 16 * kchunk;
-  const uint32_t voff = (uint32_t)(vkg * KPT) * D * 2 + 16 * vdg;
-  auto load_tile = [&](int kt) {
-    const uint32_t tile = (uint32_t)kt * BN * D * 2;
+  // LDS-direct staging: round i of wave w fills bytes i*4096 + w*1024 +
+  // 16*lane of a tile, i.e. chunk group i, rows 16w + lane/4, slice place
+  // lane % 4, which holds chunk 4i + ((lane % 4) ^ (lane / 16 % 4)) of that
+  // row.  Rows at or past N read as zero (buffer bounds).
+  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(kb, (uint32_t)N * ROWB);
+  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(vb, (uint32_t)N * ROWB);
+  const uint32_t dma_off =
+      (uint32_t)(16 * wave + (lane >> 2)) * ROWB + (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) << 4);
+  // The loads are issued from inline assembly so that the compiler, which
+  // cannot tell that they fill the other buffer, does not wait for them
+  // before every LDS read of the current one; the explicit vmcnt(0) before
+  // each barrier is their only wait.  They write no registers.
+  auto dma_tile = [&](int kt, int buf) {
 #pragma unroll
-    for (int i = 0; i < KPASS; ++i) kst[i] = buffer_ld16(krs, koff + i * RPP * D * 2, tile);
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) vst[i] = buffer_ld16(vrs, voff + i * D * 2, tile);
+    for (int i = 0; i < NDMA; ++i) {
+      const uint32_t soff = (uint32_t)kt * TILEB + i * 64;
+      const int dst = i * 4096 + wave * 1024;
+      lds_direct_ld16(krs, dma_off, soff, (char*)&Ks[buf][0] + dst);
+      lds_direct_ld16(vrs, dma_off, soff, (char*)&Vs[buf][0] + dst);
+    }
   };
-  // store_tile(buf, kt): the staged tile kt to LDS buffer buf.  With the
-  // fused handoff, rows of the query tile's diagonal key tiles that the ring
-  // keeps (positions N - S .. N - 1, slot p mod S) also go to the rings: K
-  // rows as 16-byte stores; V from the transposed registers, 4 (D = 128) or
-  // 2 (D = 64) consecutive slots of one dimension per store when they are
-  // all kept and contiguous in the ring, else one element at a time.
-  auto store_tile = [&](int buf, int kt) {
-    bool ring_now = false;
-    if constexpr (RING)
-      ring_now = kring != nullptr && kt * BN / BM == qt && (kt + 1) * BN > N - S;
-#pragma unroll
-    for (int i = 0; i < KPASS; ++i) st16(&Ks[buf][(krow0 + i * RPP) * KP + 8 * kchunk], kst[i]);
+
+  // K fragment (Q.K, tile t, k-step s): row 32t + kperm, chunk 2s + half.
+  // With kperm's row bits 2-3 fixed per lane, the byte offset is a per-lane
+  // base (one for even s, one for odd s) plus (s / 2) * 4096 + t * 2048.
+  const int kperm = 16 * (l32 >> 4) + 8 * ((l32 >> 2) & 1) + 4 * ((l32 >> 3) & 1) + (l32 & 3);
+  const int kx = (kperm >> 2) & 3;
+  const int k_even = kperm * 64 + ((half ^ kx) << 4);
+  const int k_odd = kperm * 64 + (((2 + half) ^ kx) << 4);
+  // V^T fragment (P.V step j, dim tile t): two transposed 8-byte reads, rd =
+  // 0, 1 (keys 16j + 8*(g/2) + 4rd + 0..3 of dims 32t + 16*(g%2) + i, lane =
+  // 16g + i).  Lane i of each 16-lane group points at row +i/4, dims +4(i%4).
+  const int vg = lane >> 4, vi = lane & 15;
+  const int v_lane = (8 * (vg >> 1) + (vi >> 2)) * 64 + 8 * (vi & 1);
+  const int v_c = 2 * (vg & 1) + ((vi >> 1) & 1);
+  const int v_rd0 = v_lane + ((v_c ^ ((2 * (vg >> 1)) & 3)) << 4);
+  const int v_rd1 = v_lane + ((v_c ^ ((2 * (vg >> 1) + 1) & 3)) << 4);
+
+  // Fused handoff: the tile's rows that the ring keeps (positions N - S ..
+  // N - 1, slot p mod S) go from LDS to the rings.  K: 16-byte chunks.  V:
+  // transposed reads give 4 consecutive keys of one dimension, stored as one
+  // 8-byte run when the 4 slots are consecutive (S a multiple of 4, or S = N:
+  // slot = p), else element by element.
+  auto ring_tile = [&](int kt, int buf) {
     if constexpr (RING) {
-      if (ring_now) {
+      if (kring == nullptr || kt * BN / BM != qt || (kt + 1) * BN <= N - S) return;
+      const char* kl = (const char*)&Ks[buf][0];
+      const char* vl = (const char*)&Vs[buf][0];
+      constexpr int CPR = D / 8;
 #pragma unroll
-        for (int i = 0; i < KPASS; ++i) {
-          const int p = kt * BN + krow0 + i * RPP;
-          if (p >= N - S && p < N) st16(kring + (int64_t)(p % S) * D + 8 * kchunk, kst[i]);
-        }
+      for (int u = 0; u < CPR / 4; ++u) {
+        const int id = u * 256 + tid;
+        const int r = id / CPR, c = id % CPR;
+        const int p = kt * BN + r;
+        if (p >= N - S && p < N)
+          st16(kring + (int64_t)(p % S) * D + 8 * c, *reinterpret_cast<const bf16x8*>(kl + tile_off(r, c)));
       }
-    }
-    const int vp0 = kt * BN + vkg * KPT;   // first of this thread's V keys
-    bool v_fast = false;
-    bf16* vdst = nullptr;
-    if constexpr (RING) {
-      // p0 is a multiple of KPT; with S a multiple of KPT (or S = N, slot = p)
-      // the KPT slots are consecutive and inside one 32-slot block
-      v_fast = ring_now && vp0 >= N - S && vp0 + KPT - 1 < N && (S % KPT == 0 || S == N);
-      const int slot0 = v_fast ? vp0 % S : 0;
-      vdst = vring + (int64_t)(slot0 >> 5) * (32 * D) + (8 * vdg) * 32 + (slot0 & 31);
-    }
-    u32x4 w[KPT];
+      // 16 key groups x D/16 dim blocks, one per 16-lane group and round
+      const int grp = tid >> 4;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) w[i] = __builtin_bit_cast(u32x4, vst[i]);
+      for (int u = 0; u < D / 16; ++u) {
+        const int unit = u * 16 + grp;
+        const int kg = unit & 15, m = unit >> 4;
+        const int r = 4 * kg + (vi >> 2);
+        const int dim0 = 16 * m + 4 * (vi & 3);
+        const int off = tile_off(r, dim0 >> 3) + 2 * (dim0 & 7);
+        const bf16x4 x = lds_read_tr16(vl + off);
+        const int p0 = kt * BN + 4 * kg;
+        const int d = 16 * m + vi;
+        if (p0 >= N - S && p0 + 3 < N && (S % 4 == 0 || S == N)) {
+          const int slot0 = p0 % S;
+          *reinterpret_cast<bf16x4*>(vring + (int64_t)(slot0 >> 5) * (32 * D) + d * 32 + (slot0 & 31)) = x;
+        } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      bf16* dst = &Vt[buf][(8 * vdg + e) * VP + vkg * KPT];
-      if constexpr (KPT == 4) {
-        u32x2 pk;
-        pk[0] = __builtin_amdgcn_perm(w[1][e >> 1], w[0][e >> 1], sel);
-        pk[1] = __builtin_amdgcn_perm(w[3][e >> 1], w[2][e >> 1], sel);
-        *reinterpret_cast<u32x2*>(dst) = pk;
-        if (v_fast) *reinterpret_cast<u32x2*>(vdst + 32 * e) = pk;
-      } else {
-        const uint32_t pk = __builtin_amdgcn_perm(w[1][e >> 1], w[0][e >> 1], sel);
-        *reinterpret_cast<uint32_t*>(dst) = pk;
-        if (v_fast) *reinterpret_cast<uint32_t*>(vdst + 32 * e) = pk;
-      }
-    }
-    if constexpr (RING) {
-      if (ring_now && !v_fast) {
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-          const int p = vp0 + i;
-          if (p >= N - S && p < N) {
-            const int slot = p % S;
-            bf16* d1 = vring + (int64_t)(slot >> 5) * (32 * D) + (8 * vdg) * 32 + (slot & 31);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) d1[32 * e] = vst[i][e];
+          for (int e = 0; e < 4; ++e) {
+            const int p = p0 + e;
+            if (p >= N - S && p < N) {
+              const int slot = p % S;
+              vring[(int64_t)(slot >> 5) * (32 * D) + d * 32 + (slot & 31)] = x[e];
+            }
           }
         }
       }
     }
   };
 
-  // key row of MFMA row l32 in each 32-key tile (see the file comment)
-  const int kperm = 16 * (l32 >> 4) + 8 * ((l32 >> 2) & 1) + 4 * ((l32 >> 3) & 1) + (l32 & 3);
-
-  // Double-buffered tiles: tile kt+1 is stored to LDS and tile kt+2's global
-  // loads are issued before tile kt is computed, so each load has a whole
-  // compute period to arrive; one barrier per tile.
-  load_tile(kt_lo);
-  store_tile(0, kt_lo);
-  if (kt_lo < kt_hi) load_tile(kt_lo + 1);
+  // Double-buffered LDS-direct tiles: tile kt+1's loads are issued before
+  // tile kt is computed; one wait and one barrier a tile.
+  dma_tile(kt_lo, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
   for (int kt = kt_lo; kt <= kt_hi; ++kt) {
     const int buf = (kt - kt_lo) & 1;
-    if (kt < kt_hi) {
-      store_tile(buf ^ 1, kt + 1);
-      if (kt + 1 < kt_hi) load_tile(kt + 2);
-    }
+    if (kt < kt_hi) dma_tile(kt + 1, buf ^ 1);
+    ring_tile(kt, buf);
 
     const int j0 = kt * BN;
     const bool active = iw0 < N && j0 <= iw0 + 31 && j0 + BN - 1 >= iw0 - S + 1;
     if (active) {
       const bool full = j0 + BN - 1 <= iw0 && j0 >= iw0 + 31 - S + 1 && j0 + BN <= N;
+      const char* kl = (const char*)&Ks[buf][0];
+      const char* vl = (const char*)&Vs[buf][0];
       floatx16 st[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         st[t] = minit;
-        const bf16* krow = &Ks[buf][(32 * t + kperm) * KP + 8 * half];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) st[t] = mfma32(ld16(krow + 16 * s), qop[s], st[t]);
+        for (int s = 0; s < KS; ++s) {
+          const int off = ((s & 1) ? k_odd : k_even) + (s >> 1) * 4096 + t * 2048;
+          st[t] = mfma32(*reinterpret_cast<const bf16x8*>(kl + off), qop[s], st[t]);
+        }
       }
       // keep four K-fragment reads in flight ahead of the matrix cores
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -330,19 +333,25 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
           if (i & 1) l_b = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, l_b, false);
           else       l_a = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, l_a, false);
         }
-        const bf16* vrow = &Vt[buf][l32 * VP + 16 * j + 8 * half];
 #pragma unroll
-        for (int t = 0; t < OT; ++t) acc[t] = mfma32(ld16(vrow + 32 * t * VP), pop, acc[t]);
+        for (int t = 0; t < OT; ++t) {
+          const int base = t * 4096 + 16 * j * 64;
+          const bf16x4 a0 = lds_read_tr16(vl + base + v_rd0);
+          const bf16x4 a1 = lds_read_tr16(vl + base + 4 * 64 + v_rd1);
+          const bf16x8 vop = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+          acc[t] = mfma32(vop, pop, acc[t]);
+        }
       }
       // same for the V^T fragments of the P.V product
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
 #pragma unroll
       for (int i = 0; i < 4 * OT - 4; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): tile kt+1 is in LDS
     __syncthreads();
   }
 
