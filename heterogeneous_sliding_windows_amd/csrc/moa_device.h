@@ -75,6 +75,25 @@ __device__ __forceinline__ float wave_max_xor(float x, int mask) {
   return fmaxf(x, __shfl_xor(x, mask, 64));
 }
 
+// max / sum of x over lanes l and l ^ 32 (the two wave halves), with
+// v_permlane32_swap: after it, one register holds the lower and the other
+// the upper half's value in every lane.  Written as assembly: the compiler
+// here takes the builtin's two results for one value.  The s_nop is the wait
+// a VALU write of the operands needs before the permute reads them.
+__device__ __forceinline__ void half_swap(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float half_swap_max(float x) {
+  float a = x, b = x;
+  half_swap(a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+  float a = x, b = x;
+  half_swap(a, b);
+  return a + b;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;

@@ -295,7 +295,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[t][r]);
-      mx = wave_max_xor(mx, 32);
+      mx = half_swap_max(mx);
       // Lazy rescale: the reference moves (and O, l are rescaled) only when
       // some row's tile max exceeds it by more than 8 in the exp2 domain, or
       // sets it at the row's first kept key; otherwise p <= 256, harmless in
@@ -355,8 +355,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
     __syncthreads();
   }
 
-  float l_run = l_a + l_b;
-  l_run += __shfl_xor(l_run, 32, 64);
+  const float l_run = half_swap_sum(l_a + l_b);
   if (my_q >= N) return;
   const float inv = 1.f / l_run;
   bf16* orow = ob + (int64_t)my_q * D;
