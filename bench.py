@@ -351,7 +351,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": counter_traffic(),
                      "kernel": f"moa_append_decode = decode_kernel<{w.head_dim}, true> + "
-                               f"decode_combine_kernel<{w.head_dim}>",
+                               f"decode_combine_kernel<{w.head_dim}, true>",
                      "algorithmic_bytes_per_launch": kbytes,
                      "avg_launch_ms": round(fused["decode_ms"], 4)},
         "separate_calls": {

@@ -178,8 +178,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
     float bm = sv[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) bm = fmaxf(bm, sv[e]);
-    bm = wave_max_xor(bm, 16);
-    bm = wave_max_xor(bm, 32);
+    bm = half_swap_max(row_swap_max(bm));
     // slot k0 is always valid, so bm is finite, unless it is the dropped
     // slot of a fused append: then keep the reference finite (p and alpha
     // are 0 for a block with no kept slot)
@@ -202,8 +201,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
     for (int t = 0; t < VT; ++t) acc[t] = mfma16(vop[t], pop, acc[t]);
   }
   // sum over the four lane quarters (each summed its own slots)
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
+  l_run = half_swap_sum(row_swap_sum(l_run));
 
   if constexpr (APPEND) {
     if (sub_k0 >= 0 && wave == 0) {

@@ -83,6 +83,21 @@ __device__ __forceinline__ float wave_max_xor(float x, int mask) {
 __device__ __forceinline__ void half_swap(float& a, float& b) {
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
+// Same for lanes l and l ^ 16 (v_permlane16_swap exchanges the odd and
+// even 16-lane rows).
+__device__ __forceinline__ void row_swap(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float row_swap_max(float x) {
+  float a = x, b = x;
+  row_swap(a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float row_swap_sum(float x) {
+  float a = x, b = x;
+  row_swap(a, b);
+  return a + b;
+}
 __device__ __forceinline__ float half_swap_max(float x) {
   float a = x, b = x;
   half_swap(a, b);
