@@ -212,9 +212,9 @@ class Plan:
 
     # -- inspection ---------------------------------------------------------
     def prefill_items(self):
-        """[n, 5] int32 {b (-1: every sequence), h_q, q_tile, kt_lo, kt_hi} in launch order."""
+        """[n, 6] int32 {b, h_q, q_tile, kt_lo, kt_hi, workgroup}, in workgroup order."""
         n = _check(_lib.moa_plan_prefill_items(self._h, None))
-        out = np.zeros((n, 5), dtype=np.int32)
+        out = np.zeros((n, 6), dtype=np.int32)
         _check(_lib.moa_plan_prefill_items(self._h, out.ctypes.data_as(_I32P)))
         return out
 

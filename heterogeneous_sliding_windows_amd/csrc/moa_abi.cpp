@@ -105,43 +105,77 @@ void build_ring_tables(moa_plan* p, const int64_t* alpha, const double* beta) {
   p->total_slots = total;
 }
 
-// Prefill work list: each (h_q, 128-row query tile) of a sequence with the
-// range of 64-key tiles holding at least one kept pair.  The union of the
-// windows of rows i0..i1 is the contiguous key range [max(0, i0 - S + 1), i1],
-// so the live tiles form one range.  Sorted by tile count (longest first, so
-// the tail of the launch holds the short items), ties in (b, h_q, q_tile)
-// order.  Without per-sequence lengths one list serves every sequence (the
-// launch runs item-major, sequence index fastest); otherwise the list holds
-// the items of all sequences.
+// Prefill schedule.  A work unit is 128 query rows of one (b, h_q) with the
+// range of 64-key tiles that hold a kept pair: the windows of rows i0..i1
+// together cover the contiguous keys [max(0, i0 - S + 1), i1], so the live
+// tiles form one range.  Each (b, h_q)'s units form runs of up to
+// kPrefillRun consecutive query tiles, from the last tile down (neighbouring
+// tiles read overlapping key windows, so a run's units share one XCD's L2).
+// Runs are sorted by cost (tiles plus a per-unit overhead), longest first,
+// and dealt to the 8 XCDs in groups of 8, one run per XCD, in snake order
+// (XCD 0..7 for even groups, 7..0 for odd ones) so that the XCDs' totals
+// even out.  Workgroups are dealt to the XCDs round-robin, so XCD x's k-th
+// unit sits at 8k + x; a group takes as many rounds of 8 as its longest run
+// and shorter runs are padded (bq = -1).  The 8 units of a round have about
+// the same cost, so no XCD waits long on another for its next workgroup.
 void build_prefill_items(moa_plan* p) {
-  struct Item { int32_t bq, qt, lo, hi; };
-  std::vector<Item> items;
-  const int32_t nb = p->ragged ? p->B : 1;
-  for (int32_t b = 0; b < nb; ++b) {
+  struct Unit { int32_t bq, qt, lo, hi; };
+  struct Run { int64_t cost; size_t first; int32_t n; };
+  std::vector<Unit> units;
+  std::vector<Run> runs;
+  for (int32_t b = 0; b < p->B; ++b) {
     const int64_t n = p->seq_len[b];
     const int64_t n_qt = (n + moa::kPrefillBM - 1) / moa::kPrefillBM;
     for (int32_t h = 0; h < p->Hq; ++h) {
       const int64_t s = p->span[(size_t)b * p->Hkv + h / p->G];
-      for (int64_t qt = 0; qt < n_qt; ++qt) {
-        const int64_t i0 = qt * moa::kPrefillBM;
-        const int64_t i1 = std::min<int64_t>(i0 + moa::kPrefillBM, n) - 1;
-        const int64_t j0 = std::max<int64_t>(0, i0 - s + 1);
-        items.push_back({p->ragged ? b * p->Hq + h : h, (int32_t)qt,
-                         (int32_t)(j0 / moa::kPrefillBN), (int32_t)(i1 / moa::kPrefillBN)});
+      for (int64_t top = n_qt - 1; top >= 0; top -= moa::kPrefillRun) {
+        Run r{0, units.size(), 0};
+        for (int64_t qt = top; qt >= 0 && qt > top - moa::kPrefillRun; --qt) {
+          const int64_t i0 = qt * moa::kPrefillBM;
+          const int64_t i1 = std::min<int64_t>(i0 + moa::kPrefillBM, n) - 1;
+          const int64_t j0 = std::max<int64_t>(0, i0 - s + 1);
+          const Unit u{b * p->Hq + h, (int32_t)qt, (int32_t)(j0 / moa::kPrefillBN),
+                       (int32_t)(i1 / moa::kPrefillBN)};
+          units.push_back(u);
+          r.cost += u.hi - u.lo + 1 + moa::kPrefillUnitOverhead;
+          ++r.n;
+        }
+        runs.push_back(r);
       }
     }
   }
-  std::stable_sort(items.begin(), items.end(), [](const Item& a, const Item& b) {
-    return (a.hi - a.lo) > (b.hi - b.lo);
-  });
-  p->prefill_items.resize(items.size() * 4);
-  for (size_t i = 0; i < items.size(); ++i) {
-    p->prefill_items[4 * i + 0] = items[i].bq;
-    p->prefill_items[4 * i + 1] = items[i].qt;
-    p->prefill_items[4 * i + 2] = items[i].lo;
-    p->prefill_items[4 * i + 3] = items[i].hi;
+  std::stable_sort(runs.begin(), runs.end(),
+                   [](const Run& a, const Run& b) { return a.cost > b.cost; });
+  size_t rounds = 0;
+  for (size_t g = 0; g < runs.size(); g += 8) {
+    int32_t depth = 0;
+    for (size_t r = g; r < std::min(g + 8, runs.size()); ++r) depth = std::max(depth, runs[r].n);
+    rounds += (size_t)depth;
   }
-  p->prefill_bgrid = p->ragged ? 1 : p->B;
+  p->prefill_items.assign(rounds * 8 * 4, 0);
+  for (size_t i = 0; i < rounds * 8; ++i) {
+    p->prefill_items[4 * i + 0] = -1;   // padding: the workgroup exits at once
+    p->prefill_items[4 * i + 3] = -1;
+  }
+  size_t k0 = 0;   // first round of the current group
+  for (size_t g = 0; g < runs.size(); g += 8) {
+    int32_t depth = 0;
+    for (size_t j = 0; j < 8 && g + j < runs.size(); ++j) {
+      const Run& r = runs[g + j];
+      const size_t x = (g / 8) % 2 == 0 ? j : 7 - j;
+      for (int32_t i = 0; i < r.n; ++i) {
+        const Unit& u = units[r.first + i];
+        int32_t* e = &p->prefill_items[(8 * (k0 + i) + x) * 4];
+        e[0] = u.bq;
+        e[1] = u.qt;
+        e[2] = u.lo;
+        e[3] = u.hi;
+      }
+      depth = std::max(depth, r.n);
+    }
+    k0 += (size_t)depth;
+  }
+  p->n_prefill_units = (int64_t)units.size();
 }
 
 // Decode chunk list of all sequences: each ring's S slots cut into chunks of
@@ -415,17 +449,21 @@ int64_t moa_max_batch(const moa_problem* pr, uint64_t budget_bytes) {
 int64_t moa_plan_prefill_items(moa_plan_t p, int32_t* out) {
   int st = check_plan(p, false);
   if (st != MOA_OK) return st;
-  const size_t n = p->prefill_items.size() / 4;
-  if (out)
-    for (size_t i = 0; i < n; ++i) {
-      const int32_t bq = p->prefill_items[4 * i];
-      out[5 * i + 0] = p->ragged ? bq / p->Hq : -1;
-      out[5 * i + 1] = p->ragged ? bq % p->Hq : bq;
-      out[5 * i + 2] = p->prefill_items[4 * i + 1];
-      out[5 * i + 3] = p->prefill_items[4 * i + 2];
-      out[5 * i + 4] = p->prefill_items[4 * i + 3];
+  if (out) {
+    int64_t j = 0;
+    for (size_t i = 0; i < p->prefill_items.size() / 4; ++i) {
+      const int32_t* e = &p->prefill_items[4 * i];
+      if (e[0] < 0) continue;
+      int32_t* r = out + 6 * j++;
+      r[0] = e[0] / p->Hq;
+      r[1] = e[0] % p->Hq;
+      r[2] = e[1];
+      r[3] = e[2];
+      r[4] = e[3];
+      r[5] = (int32_t)i;
     }
-  return (int64_t)n;
+  }
+  return p->n_prefill_units;
 }
 
 int64_t moa_plan_decode_chunks(moa_plan_t p, int32_t* out) {

@@ -14,9 +14,13 @@ namespace moa {
 // streamed in tiles of 64.  Both are fixed by the kernels.
 constexpr int kPrefillBM = 128;
 constexpr int kPrefillBN = 64;
-// Consecutive prefill work units each XCD runs together (measured: 16 is best
-// on both the 32-head 8k and the 64-head 64k prompts).
-constexpr int kPrefillXcdChunk = 16;
+// Prefill schedule: runs of up to kPrefillRun consecutive query tiles of one
+// (b, h_q) stay on one XCD (16 measured best on the 32-head 8k and the
+// 64-head 64k prompts); a unit's cost for balancing the XCDs is its key
+// tiles plus kPrefillUnitOverhead (its start and end, measured at about
+// three tiles' time).
+constexpr int kPrefillRun = 16;
+constexpr int kPrefillUnitOverhead = 3;
 // Default decode chunk (slots of one head's ring per workgroup).
 constexpr int kDecodeChunk = 1024;
 
@@ -24,7 +28,7 @@ struct PlanDevice {
   int32_t* span = nullptr;          // [B*Hkv] span of ring (b, h)
   int64_t* ring = nullptr;          // [B*Hkv] first slot of ring (b, h) in the pools
   int32_t* seq_len = nullptr;       // [B] prompt length of each sequence
-  int4* prefill_items = nullptr;    // [n_prefill_items] {bq, q_tile, kt_lo, kt_hi}
+  int4* prefill_items = nullptr;    // [workgroups] {b*Hq + h_q, q_tile, kt_lo, kt_hi}, bq < 0: padding
   int4* decode_chunks = nullptr;    // [n_chunks] {b*Hkv + h, first_slot, n_slots, chunks_of_ring}
   int2* head_chunks = nullptr;      // [B*Hkv] {first chunk index, chunk count}
 };
@@ -45,12 +49,10 @@ struct moa_plan {
   std::vector<int32_t> span;              // [B*Hkv]
   std::vector<int64_t> ring;              // [B*Hkv] first slot of each ring
   int64_t total_slots = 0;                // slots of all sequences' rings
-  // Prefill items, 4 per item {bq, q_tile, kt_lo, kt_hi}.  Without per-
-  // sequence lengths every sequence shares the list: bq = h_q and the launch
-  // runs each item for all B sequences (prefill_bgrid = B).  Otherwise each
-  // item is one sequence's: bq = b*Hq + h_q, prefill_bgrid = 1.
+  // Prefill launch table, 4 per workgroup {b*Hq + h_q, q_tile, kt_lo, kt_hi}
+  // (bq = -1: padding), workgroup 8k + x running XCD x's k-th unit.
   std::vector<int32_t> prefill_items;
-  int32_t prefill_bgrid = 1;
+  int64_t n_prefill_units = 0;            // table entries that are not padding
   std::vector<int32_t> decode_chunks;     // 4 per chunk, all sequences: {b*Hkv + h, first, n, chunks_of_ring}
   std::vector<int32_t> head_chunks;       // 2 per (b, h): {first chunk, count}
   int32_t decode_chunk = moa::kDecodeChunk;

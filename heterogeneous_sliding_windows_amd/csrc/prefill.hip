@@ -7,18 +7,17 @@
 // page, "Finding 2": each head has its own span, and the figure keeps a band
 // of the causal matrix.
 //
-// Work items come from the plan: 128 query rows of one h_q and the range of
-// 64-key tiles that hold at least one kept pair, longest items first; with
-// one prompt length the grid runs every item for every sequence (sequence
-// index fastest), with per-sequence lengths each item names its sequence.
-// Tiles outside the window are never loaded.  The launch order is
-// XCD-aware: each of the 8 XCDs runs runs of 16 consecutive work units, so
-// neighbouring query tiles of a head (overlapping key windows) meet in the
-// same L2 instead of being spread over all eight.  A sequence of N_b tokens
-// occupies the last N_b of the Npad rows of its [H, Npad, D] slices (left
-// padding): the kernels shift its base pointers by Npad - N_b rows and work
-// in its own positions 0 .. N_b - 1; padding rows are neither read nor
-// written.
+// Work units come from the plan's launch table: 128 query rows of one
+// (b, h_q) and the range of 64-key tiles that hold at least one kept pair;
+// tiles outside the window are never loaded.  The table is XCD-aware:
+// workgroups are dealt to the 8 XCDs round-robin, and the host lays the units
+// out so that each XCD runs runs of up to 16 consecutive query tiles of one
+// head (whose key windows overlap, so they meet in that XCD's L2), longest
+// runs first, with about the same work on every XCD.  Padding entries exit at
+// once.  A sequence of N_b tokens occupies the last N_b of the Npad rows of
+// its [H, Npad, D] slices (left padding): the kernels shift its base pointers
+// by Npad - N_b rows and work in its own positions 0 .. N_b - 1; padding rows
+// are neither read nor written.
 //
 // bf16 kernel (4 waves, 32 query rows each):
 //  * S^T = K Q^T on 32x32x16 bf16 MFMA, so each lane owns one query row and
@@ -75,9 +74,8 @@ template <int D, bool RING>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, const int4* __restrict__ items, const int32_t* __restrict__ span,
-    const int32_t* __restrict__ seq_len, int Bg, int Hq, int Hkv, int G, int Npad,
-    float scale_log2, bf16* __restrict__ kc, bf16* __restrict__ vc,
-    const int64_t* __restrict__ ring, int n_wg) {
+    const int32_t* __restrict__ seq_len, int Hq, int Hkv, int G, int Npad, float scale_log2,
+    bf16* __restrict__ kc, bf16* __restrict__ vc, const int64_t* __restrict__ ring) {
   constexpr int KS = D / 16;       // k-steps of the Q.K product
   constexpr int OT = D / 32;       // 32-dim tiles of the output
   constexpr int ROWB = D * 2;      // bytes of a K/V row
@@ -92,21 +90,9 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
   const int l32 = lane & 31;
   const int half = lane >> 5;
 
-  // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin, so the
-  // k-th workgroup of XCD x takes work unit (k / C) * 8C + x * C + k % C:
-  // each XCD runs C consecutive units (neighbouring query tiles of one head,
-  // whose key windows overlap) together and they share its L2.  The grid is
-  // padded to a multiple of 8C; the padding workgroups exit here.
-  int lin = blockIdx.x;
-  {
-    constexpr int C = kPrefillXcdChunk;
-    const int x = lin & 7, kk = lin >> 3;
-    lin = ((kk / C) * 8 + x) * C + (kk % C);
-    if (lin >= n_wg) return;
-  }
-  const int item = lin / Bg;
-  const int4 it = items[item];
-  const int b = it.x / Hq + (lin - item * Bg);
+  const int4 it = items[blockIdx.x];
+  if (it.x < 0) return;   // padding entry of the launch table
+  const int b = it.x / Hq;
   const int hq = it.x % Hq, qt = it.y, kt_lo = it.z, kt_hi = it.w;
   const int bh = b * Hq + hq;
   const int hkv = hq / G;
@@ -128,6 +114,31 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
       vring = vc + r0;
     }
   }
+
+  // LDS-direct staging: round i of wave w fills bytes i*4096 + w*1024 +
+  // 16*lane of a tile, i.e. chunk group i, rows 16w + lane/4, slice place
+  // lane % 4, which holds chunk 4i + ((lane % 4) ^ (lane / 16 % 4)) of that
+  // row.  Rows at or past N read as zero (buffer bounds).
+  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(kb, (uint32_t)N * ROWB);
+  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(vb, (uint32_t)N * ROWB);
+  const uint32_t dma_off =
+      (uint32_t)(16 * wave + (lane >> 2)) * ROWB + (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) << 4);
+  // The loads are issued from inline assembly so that the compiler, which
+  // cannot tell that they fill the other buffer, does not wait for them
+  // before every LDS read of the current one; the explicit vmcnt(0) before
+  // each barrier is their only wait.  They write no registers.
+  auto dma_tile = [&](int kt, int buf) {
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) {
+      const uint32_t soff = (uint32_t)kt * TILEB + i * 64;
+      const int dst = i * 4096 + wave * 1024;
+      lds_direct_ld16(krs, dma_off, soff, (char*)&Ks[buf][0] + dst);
+      lds_direct_ld16(vrs, dma_off, soff, (char*)&Vs[buf][0] + dst);
+    }
+  };
+
+  // the first tile's loads go out before Q's, so their latencies overlap
+  dma_tile(kt_lo, 0);
 
   const int iw0 = qt * BM + wave * 32;  // first query row of this wave
   const int my_q = iw0 + l32;
@@ -157,28 +168,6 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
   floatx16 minit;
 #pragma unroll
   for (int r = 0; r < 16; ++r) minit[r] = 0.f;
-
-  // LDS-direct staging: round i of wave w fills bytes i*4096 + w*1024 +
-  // 16*lane of a tile, i.e. chunk group i, rows 16w + lane/4, slice place
-  // lane % 4, which holds chunk 4i + ((lane % 4) ^ (lane / 16 % 4)) of that
-  // row.  Rows at or past N read as zero (buffer bounds).
-  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(kb, (uint32_t)N * ROWB);
-  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(vb, (uint32_t)N * ROWB);
-  const uint32_t dma_off =
-      (uint32_t)(16 * wave + (lane >> 2)) * ROWB + (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) << 4);
-  // The loads are issued from inline assembly so that the compiler, which
-  // cannot tell that they fill the other buffer, does not wait for them
-  // before every LDS read of the current one; the explicit vmcnt(0) before
-  // each barrier is their only wait.  They write no registers.
-  auto dma_tile = [&](int kt, int buf) {
-#pragma unroll
-    for (int i = 0; i < NDMA; ++i) {
-      const uint32_t soff = (uint32_t)kt * TILEB + i * 64;
-      const int dst = i * 4096 + wave * 1024;
-      lds_direct_ld16(krs, dma_off, soff, (char*)&Ks[buf][0] + dst);
-      lds_direct_ld16(vrs, dma_off, soff, (char*)&Vs[buf][0] + dst);
-    }
-  };
 
   // K fragment (Q.K, tile t, k-step s): row 32t + kperm, chunk 2s + half.
   // With kperm's row bits 2-3 fixed per lane, the byte offset is a per-lane
@@ -246,7 +235,6 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
 
   // Double-buffered LDS-direct tiles: tile kt+1's loads are issued before
   // tile kt is computed; one wait and one barrier a tile.
-  dma_tile(kt_lo, 0);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
   for (int kt = kt_lo; kt <= kt_hi; ++kt) {
@@ -374,17 +362,16 @@ template <int D, bool RING>
 __global__ __launch_bounds__(256) void prefill_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ o, const int4* __restrict__ items, const int32_t* __restrict__ span,
-    const int32_t* __restrict__ seq_len, int Bg, int Hq, int Hkv, int G, int Npad,
-    float scale_log2, float* __restrict__ kc, float* __restrict__ vc,
-    const int64_t* __restrict__ ring) {
+    const int32_t* __restrict__ seq_len, int Hq, int Hkv, int G, int Npad, float scale_log2,
+    float* __restrict__ kc, float* __restrict__ vc, const int64_t* __restrict__ ring) {
   constexpr int DH = D / 2;
   __shared__ __attribute__((aligned(16))) float Ks[BN * D];
   __shared__ __attribute__((aligned(16))) float Vs[BN * D];
   const int tid = threadIdx.x;
   const int half = tid & 1;
-  const int item = blockIdx.x / Bg;
-  const int4 it = items[item];
-  const int b = it.x / Hq + (blockIdx.x - item * Bg);
+  const int4 it = items[blockIdx.x];
+  if (it.x < 0) return;   // padding entry of the launch table
+  const int b = it.x / Hq;
   const int hq = it.x % Hq, qt = it.y, kt_lo = it.z, kt_hi = it.w;
   const int bh = b * Hq + hq;
   const int hkv = hq / G;
@@ -486,28 +473,25 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
 template <int D, bool RING>
 void launch_bf16(const moa_plan& p, const void* q, const void* k, const void* v, void* o, void* kc,
                  void* vc, hipStream_t s) {
-  const unsigned n_items = (unsigned)(p.prefill_items.size() / 4 * p.prefill_bgrid);
+  const unsigned grid = (unsigned)(p.prefill_items.size() / 4);
   const float scale_log2 = kLog2e / sqrtf((float)D);
-  constexpr unsigned round = 8 * kPrefillXcdChunk;
-  const unsigned grid = (n_items + round - 1) / round * round;
   hipLaunchKernelGGL((prefill_bf16_kernel<D, RING>), dim3(grid), dim3(256), 0, s,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                      static_cast<const bf16*>(v), static_cast<bf16*>(o), p.dev.prefill_items,
-                     p.dev.span, p.dev.seq_len, p.prefill_bgrid, p.Hq, p.Hkv, p.G, (int)p.N,
-                     scale_log2, static_cast<bf16*>(kc), static_cast<bf16*>(vc), p.dev.ring,
-                     (int)n_items);
+                     p.dev.span, p.dev.seq_len, p.Hq, p.Hkv, p.G, (int)p.N, scale_log2,
+                     static_cast<bf16*>(kc), static_cast<bf16*>(vc), p.dev.ring);
 }
 
 template <int D, bool RING>
 void launch_f32(const moa_plan& p, const void* q, const void* k, const void* v, void* o, void* kc,
                 void* vc, hipStream_t s) {
-  const unsigned n_items = (unsigned)(p.prefill_items.size() / 4 * p.prefill_bgrid);
+  const unsigned grid = (unsigned)(p.prefill_items.size() / 4);
   const float scale_log2 = kLog2e / sqrtf((float)D);
-  hipLaunchKernelGGL((prefill_f32_kernel<D, RING>), dim3(n_items), dim3(256), 0, s,
+  hipLaunchKernelGGL((prefill_f32_kernel<D, RING>), dim3(grid), dim3(256), 0, s,
                      static_cast<const float*>(q), static_cast<const float*>(k),
                      static_cast<const float*>(v), static_cast<float*>(o), p.dev.prefill_items,
-                     p.dev.span, p.dev.seq_len, p.prefill_bgrid, p.Hq, p.Hkv, p.G, (int)p.N,
-                     scale_log2, static_cast<float*>(kc), static_cast<float*>(vc), p.dev.ring);
+                     p.dev.span, p.dev.seq_len, p.Hq, p.Hkv, p.G, (int)p.N, scale_log2,
+                     static_cast<float*>(kc), static_cast<float*>(vc), p.dev.ring);
 }
 
 }  // namespace

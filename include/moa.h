@@ -176,13 +176,18 @@ size_t moa_decode_workspace_bytes(moa_plan_t plan);
  * moa_plan_create). */
 int64_t moa_max_batch(const moa_problem* problem, uint64_t budget_bytes);
 
-/* Work-list inspection, for tests.  Prefill items are int32 quintuples
- * {b, h_q, q_tile, kt_lo, kt_hi}: query rows q_tile*128 .. +127 of sequence
- * b (its own positions) read key tiles kt_lo .. kt_hi (64 keys each), i.e.
- * every tile holding at least one kept (query, key) pair and no other; b = -1
- * marks an item of a plan without per-sequence lengths, which the launch
- * runs for every sequence in turn.  Items are in launch order: cost
- * (kt_hi - kt_lo + 1) descending, ties in list order (b, h_q, q_tile).
+/* Work-list inspection, for tests.  Prefill items are int32 sextuples
+ * {b, h_q, q_tile, kt_lo, kt_hi, wg}: query rows q_tile*128 .. +127 of
+ * sequence b (its own positions) read key tiles kt_lo .. kt_hi (64 keys
+ * each), i.e. every tile holding at least one kept (query, key) pair and no
+ * other, in workgroup wg of the launch; items are listed in wg order.  The
+ * schedule: each (b, h_q)'s query tiles form runs of up to 16 consecutive
+ * tiles, from its last tile down; runs are sorted by cost (the units' tile
+ * counts plus 3 per unit), longest first, equal costs in (b, h_q, run)
+ * order; groups of 8 consecutive runs go one run per XCD, XCD j for the j-th
+ * run of an even group and 7 - j of an odd one; XCD x's k-th unit runs in
+ * workgroup 8k + x, and a group spans as many rounds of 8 workgroups as its
+ * longest run.  Workgroup numbers missing from the list are padding.
  * Decode chunks are int32 quadruples {b, h_kv, first_slot, n_slots} of all
  * sequences, in launch order; each ring is cut into chunks of at most
  * moa_plan_decode_chunk() slots.  Pass out = NULL to get the count; the

@@ -87,12 +87,12 @@ def test_workload_plan_tables(moa, name):
 
 
 def _check_prefill_items(items, n, n_q_heads, span_of_q):
-    """Items {b, h_q, q_tile, kt_lo, kt_hi} of one sequence with n tokens: each (h_q, q_tile)
+    """Items {b, h_q, q_tile, kt_lo, kt_hi, wg} of one sequence with n tokens: each (h_q, q_tile)
     once; [kt_lo, kt_hi] = exactly the live 64-key tiles of the oracle's mask rows."""
     n_qt = (n + 127) // 128
     assert len(items) == n_q_heads * n_qt
     seen = set()
-    for _, hq, qt, lo, hi in items:
+    for _, hq, qt, lo, hi, _ in items:
         assert (hq, qt) not in seen
         seen.add((hq, qt))
         s = span_of_q(hq)
@@ -103,13 +103,36 @@ def _check_prefill_items(items, n, n_q_heads, span_of_q):
         assert live == list(range(lo, hi + 1)), (hq, qt, lo, hi, live[:3], live[-3:])
 
 
-def _check_lpt_order(items):
-    """Launch order: cost descending, ties in list order (b, h_q, q_tile)."""
-    cost = items[:, 4] - items[:, 3]
-    assert (np.diff(cost) <= 0).all()
-    for i in range(1, len(items)):
-        if cost[i] == cost[i - 1]:
-            assert tuple(items[i, :3]) > tuple(items[i - 1, :3])
+def _check_schedule(items):
+    """Workgroup order of the launch table, rebuilt from its stated rule: runs of up to 16
+    consecutive query tiles of one (b, h_q) from the last tile down; runs longest first
+    (tiles + 3 per unit; ties in (b, h_q, run) order); groups of 8 runs, one per XCD in
+    snake order; XCD x's k-th unit in workgroup 8k + x, a group as deep as its longest run."""
+    key = {tuple(r[:3]): r for r in items}
+    tiles = {}
+    for b, hq, qt in key:
+        tiles.setdefault((b, hq), []).append(qt)
+    runs = []
+    for b, hq in sorted(tiles):
+        qts = sorted(tiles[(b, hq)], reverse=True)
+        assert qts == list(range(len(qts) - 1, -1, -1))
+        for i in range(0, len(qts), 16):
+            run = [(b, hq, t) for t in qts[i:i + 16]]
+            runs.append((sum(key[u][4] - key[u][3] + 1 + 3 for u in run), len(runs), run))
+    runs.sort(key=lambda r: (-r[0], r[1]))
+    want, k0, load = [], 0, [0] * 8
+    for g in range(0, len(runs), 8):
+        group = runs[g:g + 8]
+        for j, (cost, _, run) in enumerate(group):
+            x = j if (g // 8) % 2 == 0 else 7 - j
+            want += [(8 * (k0 + i) + x, u) for i, u in enumerate(run)]
+            load[x] += cost
+        k0 += max(len(r[2]) for r in group)
+    want.sort()
+    assert [w for w, _ in want] == list(items[:, 5])
+    assert [u for _, u in want] == [tuple(r[:3]) for r in items]
+    # snake dealing keeps the XCDs' totals within the costliest run of each other
+    assert max(load) - min(load) <= max(r[0] for r in runs)
 
 
 @pytest.mark.parametrize("n,alpha,beta,hq,hkv", [
@@ -123,9 +146,9 @@ def test_prefill_items_bruteforce(moa, n, alpha, beta, hq, hkv):
     s = oracle.spans(alpha, beta, n)
     g = hq // hkv
     items = plan.prefill_items()
-    assert (items[:, 0] == -1).all()          # one list serves every sequence
-    _check_prefill_items(items, n, hq, lambda h: int(s[h // g]))
-    _check_lpt_order(items)
+    for b in range(2):                        # both sequences' units, each once
+        _check_prefill_items(items[items[:, 0] == b], n, hq, lambda h: int(s[h // g]))
+    _check_schedule(items)
 
 
 def test_prefill_items_full_size_tables(moa):
@@ -142,7 +165,7 @@ def test_prefill_items_full_size_tables(moa):
         j = np.arange(n)
         rng = np.random.Generator(np.random.PCG64(3))
         for idx in rng.integers(0, len(items), 200):
-            _, hq, qt, lo, hi = items[idx]
+            _, hq, qt, lo, hi, _ = items[idx]
             sp = int(s[hq // g])
             r0, r1 = qt * 128, min(qt * 128 + 128, n) - 1
             kept = np.zeros(n, dtype=bool)
@@ -151,6 +174,7 @@ def test_prefill_items_full_size_tables(moa):
             kept[max(0, r0 - sp + 1):r1 + 1] = True
             tiles = np.nonzero(kept.reshape(-1, 64).any(axis=1))[0]
             assert (tiles.min(), tiles.max()) == (lo, hi)
+        _check_schedule(items)
         plan.close()
 
 
@@ -350,7 +374,7 @@ def test_ragged_prefill_items_bruteforce(moa, case):
         s = oracle.spans(alpha, beta, nb)
         _check_prefill_items(items[items[:, 0] == b], nb, hq, lambda h: int(s[h // g]))
     assert set(items[:, 0]) == set(range(len(lens)))
-    _check_lpt_order(items)
+    _check_schedule(items)
     plan.close()
 
 
