@@ -116,14 +116,18 @@ void build_ring_tables(moa_plan* p, const int64_t* alpha, const double* beta) {
 // (XCD 0..7 for even groups, 7..0 for odd ones) so that the XCDs' totals
 // even out.  Workgroups are dealt to the XCDs round-robin, so XCD x's k-th
 // unit sits at 8k + x; a group takes as many rounds of 8 as its longest run
-// and shorter runs are padded (bq = -1).  The 8 units of a round have about
-// the same cost, so no XCD waits long on another for its next workgroup.
+// and shorter runs are padded (bq = -1).  With one prompt length every
+// sequence has the same units, so the table is built for sequence 0 and the
+// launch runs it once per sequence (its length is a multiple of 8, so each
+// copy keeps the XCD assignment); with per-sequence lengths the table holds
+// every sequence's units.
 void build_prefill_items(moa_plan* p) {
   struct Unit { int32_t bq, qt, lo, hi; };
   struct Run { int64_t cost; size_t first; int32_t n; };
   std::vector<Unit> units;
   std::vector<Run> runs;
-  for (int32_t b = 0; b < p->B; ++b) {
+  const int32_t nb = p->ragged ? p->B : 1;
+  for (int32_t b = 0; b < nb; ++b) {
     const int64_t n = p->seq_len[b];
     const int64_t n_qt = (n + moa::kPrefillBM - 1) / moa::kPrefillBM;
     for (int32_t h = 0; h < p->Hq; ++h) {
@@ -175,7 +179,8 @@ void build_prefill_items(moa_plan* p) {
     }
     k0 += (size_t)depth;
   }
-  p->n_prefill_units = (int64_t)units.size();
+  p->prefill_seq_grid = p->ragged ? 0 : (int64_t)rounds * 8;
+  p->n_prefill_units = (int64_t)units.size() * (p->ragged ? 1 : p->B);
 }
 
 // Decode chunk list of all sequences: each ring's S slots cut into chunks of
@@ -228,6 +233,9 @@ int check_prefill(moa_plan_t p, const void* q, const void* k, const void* v, con
   if (!q || !k || !v || !o) return fail(MOA_EINVAL, "%s: q, k, v and o must not be NULL", who);
   if (p->N * p->D * (p->dtype == MOA_BF16 ? 2 : 4) >= ((int64_t)1 << 31))
     return fail(MOA_EUNSUPPORTED, "%s: one head's K/V (N x head_dim) must stay below 2 GiB", who);
+  const uint64_t table = p->prefill_items.size() / 4;
+  if ((p->prefill_seq_grid > 0 ? table * (uint64_t)p->B : table) > 0xFFFFFFFFull)
+    return fail(MOA_EUNSUPPORTED, "%s: the prefill launch needs more than 2^32 - 1 workgroups", who);
   return set_device(p);
 }
 
@@ -450,18 +458,21 @@ int64_t moa_plan_prefill_items(moa_plan_t p, int32_t* out) {
   int st = check_plan(p, false);
   if (st != MOA_OK) return st;
   if (out) {
+    const int64_t T = (int64_t)p->prefill_items.size() / 4;
+    const int32_t copies = p->prefill_seq_grid > 0 ? p->B : 1;
     int64_t j = 0;
-    for (size_t i = 0; i < p->prefill_items.size() / 4; ++i) {
-      const int32_t* e = &p->prefill_items[4 * i];
-      if (e[0] < 0) continue;
-      int32_t* r = out + 6 * j++;
-      r[0] = e[0] / p->Hq;
-      r[1] = e[0] % p->Hq;
-      r[2] = e[1];
-      r[3] = e[2];
-      r[4] = e[3];
-      r[5] = (int32_t)i;
-    }
+    for (int32_t c = 0; c < copies; ++c)
+      for (int64_t i = 0; i < T; ++i) {
+        const int32_t* e = &p->prefill_items[4 * i];
+        if (e[0] < 0) continue;
+        int32_t* r = out + 6 * j++;
+        r[0] = e[0] / p->Hq + c;
+        r[1] = e[0] % p->Hq;
+        r[2] = e[1];
+        r[3] = e[2];
+        r[4] = e[3];
+        r[5] = (int32_t)(c * T + i);
+      }
   }
   return p->n_prefill_units;
 }

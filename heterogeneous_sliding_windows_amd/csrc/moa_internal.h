@@ -28,7 +28,7 @@ struct PlanDevice {
   int32_t* span = nullptr;          // [B*Hkv] span of ring (b, h)
   int64_t* ring = nullptr;          // [B*Hkv] first slot of ring (b, h) in the pools
   int32_t* seq_len = nullptr;       // [B] prompt length of each sequence
-  int4* prefill_items = nullptr;    // [workgroups] {b*Hq + h_q, q_tile, kt_lo, kt_hi}, bq < 0: padding
+  int4* prefill_items = nullptr;    // launch table {b*Hq + h_q, q_tile, kt_lo, kt_hi}, bq < 0: padding
   int4* decode_chunks = nullptr;    // [n_chunks] {b*Hkv + h, first_slot, n_slots, chunks_of_ring}
   int2* head_chunks = nullptr;      // [B*Hkv] {first chunk index, chunk count}
 };
@@ -49,10 +49,15 @@ struct moa_plan {
   std::vector<int32_t> span;              // [B*Hkv]
   std::vector<int64_t> ring;              // [B*Hkv] first slot of each ring
   int64_t total_slots = 0;                // slots of all sequences' rings
-  // Prefill launch table, 4 per workgroup {b*Hq + h_q, q_tile, kt_lo, kt_hi}
-  // (bq = -1: padding), workgroup 8k + x running XCD x's k-th unit.
+  // Prefill launch table, 4 per entry {b*Hq + h_q, q_tile, kt_lo, kt_hi}
+  // (bq = -1: padding), entry 8k + x running XCD x's k-th unit.  Without
+  // per-sequence lengths the table holds one sequence's units (b = 0) and the
+  // launch runs it for every sequence in turn: workgroup b * prefill_seq_grid
+  // + e runs entry e for sequence b.  Otherwise it lists every sequence's
+  // units and prefill_seq_grid is 0.
   std::vector<int32_t> prefill_items;
-  int64_t n_prefill_units = 0;            // table entries that are not padding
+  int64_t prefill_seq_grid = 0;
+  int64_t n_prefill_units = 0;            // units of all sequences
   std::vector<int32_t> decode_chunks;     // 4 per chunk, all sequences: {b*Hkv + h, first, n, chunks_of_ring}
   std::vector<int32_t> head_chunks;       // 2 per (b, h): {first chunk, count}
   int32_t decode_chunk = moa::kDecodeChunk;

@@ -74,8 +74,9 @@ template <int D, bool RING>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, const int4* __restrict__ items, const int32_t* __restrict__ span,
-    const int32_t* __restrict__ seq_len, int Hq, int Hkv, int G, int Npad, float scale_log2,
-    bf16* __restrict__ kc, bf16* __restrict__ vc, const int64_t* __restrict__ ring) {
+    const int32_t* __restrict__ seq_len, int seq_grid, int Hq, int Hkv, int G, int Npad,
+    float scale_log2, bf16* __restrict__ kc, bf16* __restrict__ vc,
+    const int64_t* __restrict__ ring) {
   constexpr int KS = D / 16;       // k-steps of the Q.K product
   constexpr int OT = D / 32;       // 32-dim tiles of the output
   constexpr int ROWB = D * 2;      // bytes of a K/V row
@@ -90,9 +91,11 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
   const int l32 = lane & 31;
   const int half = lane >> 5;
 
-  const int4 it = items[blockIdx.x];
+  // the table runs once per sequence (seq_grid > 0) or names the sequence
+  const unsigned copy = seq_grid > 0 ? blockIdx.x / (unsigned)seq_grid : 0u;
+  const int4 it = items[blockIdx.x - copy * (unsigned)seq_grid];
   if (it.x < 0) return;   // padding entry of the launch table
-  const int b = it.x / Hq;
+  const int b = it.x / Hq + (int)copy;
   const int hq = it.x % Hq, qt = it.y, kt_lo = it.z, kt_hi = it.w;
   const int bh = b * Hq + hq;
   const int hkv = hq / G;
@@ -368,16 +371,19 @@ template <int D, bool RING>
 __global__ __launch_bounds__(256) void prefill_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ o, const int4* __restrict__ items, const int32_t* __restrict__ span,
-    const int32_t* __restrict__ seq_len, int Hq, int Hkv, int G, int Npad, float scale_log2,
-    float* __restrict__ kc, float* __restrict__ vc, const int64_t* __restrict__ ring) {
+    const int32_t* __restrict__ seq_len, int seq_grid, int Hq, int Hkv, int G, int Npad,
+    float scale_log2, float* __restrict__ kc, float* __restrict__ vc,
+    const int64_t* __restrict__ ring) {
   constexpr int DH = D / 2;
   __shared__ __attribute__((aligned(16))) float Ks[BN * D];
   __shared__ __attribute__((aligned(16))) float Vs[BN * D];
   const int tid = threadIdx.x;
   const int half = tid & 1;
-  const int4 it = items[blockIdx.x];
+  // the table runs once per sequence (seq_grid > 0) or names the sequence
+  const unsigned copy = seq_grid > 0 ? blockIdx.x / (unsigned)seq_grid : 0u;
+  const int4 it = items[blockIdx.x - copy * (unsigned)seq_grid];
   if (it.x < 0) return;   // padding entry of the launch table
-  const int b = it.x / Hq;
+  const int b = it.x / Hq + (int)copy;
   const int hq = it.x % Hq, qt = it.y, kt_lo = it.z, kt_hi = it.w;
   const int bh = b * Hq + hq;
   const int hkv = hq / G;
@@ -479,24 +485,28 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
 template <int D, bool RING>
 void launch_bf16(const moa_plan& p, const void* q, const void* k, const void* v, void* o, void* kc,
                  void* vc, hipStream_t s) {
-  const unsigned grid = (unsigned)(p.prefill_items.size() / 4);
+  const unsigned table = (unsigned)(p.prefill_items.size() / 4);
+  const unsigned grid = p.prefill_seq_grid > 0 ? table * (unsigned)p.B : table;
   const float scale_log2 = kLog2e / sqrtf((float)D);
   hipLaunchKernelGGL((prefill_bf16_kernel<D, RING>), dim3(grid), dim3(256), 0, s,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                      static_cast<const bf16*>(v), static_cast<bf16*>(o), p.dev.prefill_items,
-                     p.dev.span, p.dev.seq_len, p.Hq, p.Hkv, p.G, (int)p.N, scale_log2,
+                     p.dev.span, p.dev.seq_len, (int)p.prefill_seq_grid, p.Hq, p.Hkv, p.G, (int)p.N,
+                     scale_log2,
                      static_cast<bf16*>(kc), static_cast<bf16*>(vc), p.dev.ring);
 }
 
 template <int D, bool RING>
 void launch_f32(const moa_plan& p, const void* q, const void* k, const void* v, void* o, void* kc,
                 void* vc, hipStream_t s) {
-  const unsigned grid = (unsigned)(p.prefill_items.size() / 4);
+  const unsigned table = (unsigned)(p.prefill_items.size() / 4);
+  const unsigned grid = p.prefill_seq_grid > 0 ? table * (unsigned)p.B : table;
   const float scale_log2 = kLog2e / sqrtf((float)D);
   hipLaunchKernelGGL((prefill_f32_kernel<D, RING>), dim3(grid), dim3(256), 0, s,
                      static_cast<const float*>(q), static_cast<const float*>(k),
                      static_cast<const float*>(v), static_cast<float*>(o), p.dev.prefill_items,
-                     p.dev.span, p.dev.seq_len, p.Hq, p.Hkv, p.G, (int)p.N, scale_log2,
+                     p.dev.span, p.dev.seq_len, (int)p.prefill_seq_grid, p.Hq, p.Hkv, p.G, (int)p.N,
+                     scale_log2,
                      static_cast<float*>(kc), static_cast<float*>(vc), p.dev.ring);
 }
 

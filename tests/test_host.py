@@ -103,11 +103,12 @@ def _check_prefill_items(items, n, n_q_heads, span_of_q):
         assert live == list(range(lo, hi + 1)), (hq, qt, lo, hi, live[:3], live[-3:])
 
 
-def _check_schedule(items):
-    """Workgroup order of the launch table, rebuilt from its stated rule: runs of up to 16
-    consecutive query tiles of one (b, h_q) from the last tile down; runs longest first
-    (tiles + 3 per unit; ties in (b, h_q, run) order); groups of 8 runs, one per XCD in
-    snake order; XCD x's k-th unit in workgroup 8k + x, a group as deep as its longest run."""
+def _schedule_of(items):
+    """Workgroup order rebuilt from the stated rule: runs of up to 16 consecutive query tiles
+    of one (b, h_q) from the last tile down; runs longest first (tiles + 3 per unit; ties in
+    (b, h_q, run) order); groups of 8 runs, one per XCD in snake order; XCD x's k-th unit in
+    workgroup 8k + x, a group as deep as its longest run.  Returns ({unit: wg}, table length,
+    XCD loads, the costliest run)."""
     key = {tuple(r[:3]): r for r in items}
     tiles = {}
     for b, hq, qt in key:
@@ -120,19 +121,29 @@ def _check_schedule(items):
             run = [(b, hq, t) for t in qts[i:i + 16]]
             runs.append((sum(key[u][4] - key[u][3] + 1 + 3 for u in run), len(runs), run))
     runs.sort(key=lambda r: (-r[0], r[1]))
-    want, k0, load = [], 0, [0] * 8
+    wg, k0, load = {}, 0, [0] * 8
     for g in range(0, len(runs), 8):
         group = runs[g:g + 8]
         for j, (cost, _, run) in enumerate(group):
             x = j if (g // 8) % 2 == 0 else 7 - j
-            want += [(8 * (k0 + i) + x, u) for i, u in enumerate(run)]
+            wg.update({u: 8 * (k0 + i) + x for i, u in enumerate(run)})
             load[x] += cost
         k0 += max(len(r[2]) for r in group)
-    want.sort()
-    assert [w for w, _ in want] == list(items[:, 5])
-    assert [u for _, u in want] == [tuple(r[:3]) for r in items]
+    return wg, 8 * k0, load, max(r[0] for r in runs)
+
+
+def _check_schedule(items, per_sequence_lengths):
+    """The launch table follows its stated rule: over all sequences' units for a plan with
+    per-sequence lengths; otherwise sequence 0's table, run once per sequence."""
+    assert list(items[:, 5]) == sorted(items[:, 5]) and len(set(items[:, 5])) == len(items)
+    if per_sequence_lengths:
+        wg, _, load, top = _schedule_of(items)
+    else:
+        wg0, t, load, top = _schedule_of(items[items[:, 0] == 0])
+        wg = {(b, hq, qt): b * t + wg0[(0, hq, qt)] for b, hq, qt in (tuple(r[:3]) for r in items)}
+    assert [wg[tuple(r[:3])] for r in items] == list(items[:, 5])
     # snake dealing keeps the XCDs' totals within the costliest run of each other
-    assert max(load) - min(load) <= max(r[0] for r in runs)
+    assert max(load) - min(load) <= top
 
 
 @pytest.mark.parametrize("n,alpha,beta,hq,hkv", [
@@ -148,7 +159,7 @@ def test_prefill_items_bruteforce(moa, n, alpha, beta, hq, hkv):
     items = plan.prefill_items()
     for b in range(2):                        # both sequences' units, each once
         _check_prefill_items(items[items[:, 0] == b], n, hq, lambda h: int(s[h // g]))
-    _check_schedule(items)
+    _check_schedule(items, False)
 
 
 def test_prefill_items_full_size_tables(moa):
@@ -174,7 +185,7 @@ def test_prefill_items_full_size_tables(moa):
             kept[max(0, r0 - sp + 1):r1 + 1] = True
             tiles = np.nonzero(kept.reshape(-1, 64).any(axis=1))[0]
             assert (tiles.min(), tiles.max()) == (lo, hi)
-        _check_schedule(items)
+        _check_schedule(items, False)
         plan.close()
 
 
@@ -374,7 +385,7 @@ def test_ragged_prefill_items_bruteforce(moa, case):
         s = oracle.spans(alpha, beta, nb)
         _check_prefill_items(items[items[:, 0] == b], nb, hq, lambda h: int(s[h // g]))
     assert set(items[:, 0]) == set(range(len(lens)))
-    _check_schedule(items)
+    _check_schedule(items, True)
     plan.close()
 
 
