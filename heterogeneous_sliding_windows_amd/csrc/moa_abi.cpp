@@ -322,6 +322,11 @@ int create_plan(const moa_problem* pr, const int64_t* seq_len, uint32_t flags, m
     if (seq_len) std::copy(seq_len, seq_len + p->B, p->seq_len.begin());
     build_ring_tables(p, pr->alpha, pr->beta);
     build_prefill_items(p);
+    p->decode_chunk = moa::decode_chunk_for(p->G, [&](int c) {
+      int64_t n = 0;
+      for (const int32_t sp : p->span) n += (sp + c - 1) / c;
+      return n;
+    });
     build_decode_chunks(p);
   } catch (const std::bad_alloc&) {
     delete p;
@@ -442,13 +447,23 @@ int64_t moa_max_batch(const moa_problem* pr, uint64_t budget_bytes) {
   // reports for batch B; the largest B with bytes(B) <= budget
   const uint64_t elem = p->dtype == MOA_BF16 ? 2 : 4;
   const uint64_t cache = 2ull * (uint64_t)p->total_slots * (uint64_t)p->D * elem;
-  const uint64_t ws = (uint64_t)p->n_chunks * (uint64_t)p->G * ((uint64_t)p->D + 2) * 4ull;
+  const int G = p->G;
+  const uint64_t row = (uint64_t)G * ((uint64_t)p->D + 2) * 4ull;   // partial bytes per chunk
+  const std::vector<int32_t> span = p->span;
   moa_plan_destroy(p);
+  // chunks of one sequence's rings at chunk size c
+  auto per_seq = [&](int c) {
+    uint64_t n = 0;
+    for (const int32_t sp : span) n += (uint64_t)((sp + c - 1) / c);
+    return n;
+  };
+  // the workspace of batch b uses the chunk size a plan of batch b would take
   auto bytes = [&](uint64_t b) {
-    uint64_t w = (b * ws + 255) & ~(uint64_t)255;
+    const int c = moa::decode_chunk_for(G, [&](int cc) { return (int64_t)(b * per_seq(cc)); });
+    uint64_t w = (b * per_seq(c) * row + 255) & ~(uint64_t)255;
     return b * cache + (w < 256 ? 256 : w);
   };
-  uint64_t b = budget_bytes / (cache + ws);
+  uint64_t b = budget_bytes / (cache + per_seq(moa::kDecodeChunk) * row);
   while (b > 0 && bytes(b) > budget_bytes) --b;
   while (bytes(b + 1) <= budget_bytes) ++b;
   return (int64_t)b;

@@ -21,8 +21,22 @@ constexpr int kPrefillBN = 64;
 // three tiles' time).
 constexpr int kPrefillRun = 16;
 constexpr int kPrefillUnitOverhead = 3;
-// Default decode chunk (slots of one head's ring per workgroup).
+// Decode chunk (slots of one head's ring per workgroup) for ungrouped heads.
 constexpr int kDecodeChunk = 1024;
+// A chunk of a KV group publishes G partial rows, and those writes, mixed
+// into a read stream near the HBM limit, cost far more than their bytes; so a
+// plan with G > 1 takes the largest of these sizes that still leaves
+// kDecodeMinChunks chunks (four rounds of the 512 workgroups MI355X holds).
+constexpr int kDecodeGroupChunks[4] = {3072, 2048, 1536, 1024};
+constexpr int64_t kDecodeMinChunks = 2048;
+// The chunk size of a plan; chunks_at(c) = chunks of all its rings at size c.
+template <class F>
+int decode_chunk_for(int G, F chunks_at) {
+  if (G > 1)
+    for (int c : kDecodeGroupChunks)
+      if (chunks_at(c) >= kDecodeMinChunks) return c;
+  return kDecodeChunk;
+}
 
 struct PlanDevice {
   int32_t* span = nullptr;          // [B*Hkv] span of ring (b, h)

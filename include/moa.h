@@ -193,7 +193,9 @@ int64_t moa_max_batch(const moa_problem* problem, uint64_t budget_bytes);
  * sequence: sequence b's unit at entry e runs in workgroup b*T + e.
  * Decode chunks are int32 quadruples {b, h_kv, first_slot, n_slots} of all
  * sequences, in launch order; each ring is cut into chunks of at most
- * moa_plan_decode_chunk() slots.  Pass out = NULL to get the count; the
+ * moa_plan_decode_chunk() slots: 1024 when G = 1, else the largest of 3072,
+ * 2048, 1536 that still gives the plan at least 2048 chunks (1024 if none
+ * does).  Pass out = NULL to get the count; the
  * return value is the item count (>= 0) or a negative moa_status. */
 int64_t moa_plan_prefill_items(moa_plan_t plan, int32_t* out);
 int64_t moa_plan_decode_chunks(moa_plan_t plan, int32_t* out);

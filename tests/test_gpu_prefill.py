@@ -49,6 +49,7 @@ CASES = [
     (2, 16, 2, 128, 300, [0, 0], [0.0, 1.0], "bf16"),
     (1, 2, 1, 128, 1, [0], [1.0], "bf16"),
     (1, 2, 2, 128, 130, [64, 0], [0.0, 0.0], "bf16"),
+    (5, 4, 2, 128, 700, [0, 300], [0.5, 0.0], "bf16"),
     (2, 4, 2, 64, 333, [0, 200], [0.5, 0.0], "f32"),
     (1, 2, 2, 128, 257, [0, 64], [1.0, 0.0], "f32"),
 ]

@@ -189,6 +189,24 @@ def test_prefill_items_full_size_tables(moa):
         plan.close()
 
 
+@pytest.mark.parametrize("batch,hq,hkv,n", [
+    (64, 32, 32, 16384), (16, 64, 8, 65536), (8, 64, 8, 65536), (64, 256, 32, 16384),
+    (1, 8, 2, 1000), (2000, 8, 1, 4096)])
+def test_decode_chunk_rule(moa, batch, hq, hkv, n):
+    """1024 slots for ungrouped heads; with G > 1 the largest of 3072, 2048, 1536 that leaves
+    at least 2048 chunks, else 1024 (the rule include/moa.h states)."""
+    alpha, beta = workloads.rules("c4_decode")
+    alpha, beta = (list(alpha) * 8)[:hkv], (list(beta) * 8)[:hkv]
+    plan = moa.Plan(batch, hq, hkv, 128, n, alpha, beta, host_only=True)
+    s = np.tile(oracle.spans(alpha, beta, n), batch)
+    want = 1024
+    if hq // hkv > 1:
+        want = next((c for c in (3072, 2048, 1536) if int(np.sum((s + c - 1) // c)) >= 2048), 1024)
+    assert plan.decode_chunk == want
+    assert len(plan.decode_chunks()) == int(np.sum((s + want - 1) // want))
+    plan.close()
+
+
 @pytest.mark.parametrize("name", ["c2_decode", "c3_decode", "c4_decode"])
 def test_decode_chunks_cover_rings(moa, name):
     w = workloads.WORKLOADS[name]
