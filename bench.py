@@ -288,8 +288,10 @@ def main():
                          "known-size kernel that scales the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the attention path has "
-              "no cross-GPU step here; see DESIGN.md for how it would shard.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): heads and sequences "
+              "never interact in attention, so a multi-GPU run would shard KV-head groups or "
+              "sequences with no exchange inside the path, and none is built here.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
