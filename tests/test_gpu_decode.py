@@ -135,12 +135,21 @@ def test_decode_argument_errors(moa):
         plan.decode(q[:, :1], kc, vc, 64, o, plan.new_workspace())
 
 
-@pytest.mark.parametrize("name", ["c2_decode", "c3_decode", "c4_decode"])
+# Grouped heads at a size where the plan takes 3072-slot chunks (the rule of
+# moa_plan_decode_chunk): B64 Hq64 Hkv8 D128 N24576 with the 64-head 64k rules.
+GQA_3072 = workloads.Workload("gqa_chunk3072", "decode", 64, 64, 8, 128, 24576, "bf16", 3, "c4",
+                              2005, "B64 Hq64 Hkv8 D128 N24576 bf16, 3072-slot decode chunks")
+
+
+@pytest.mark.parametrize("name", ["c2_decode", "c3_decode", "c4_decode", "gqa_chunk3072"])
 def test_decode_full_size_sampled_heads(moa, name):
     """Full-size rings (device-filled with seeded N(0,1)), a few steps, sampled (b, h) checked."""
-    w = workloads.WORKLOADS[name]
-    alpha, beta = workloads.rules(name)
+    w = GQA_3072 if name == "gqa_chunk3072" else workloads.WORKLOADS[name]
+    alpha, beta = workloads.rules("c4_decode" if name == "gqa_chunk3072" else name)
     plan = moa.Plan(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, alpha, beta)
+    log(f"{name}: decode chunk {plan.decode_chunk} slots, {len(plan.decode_chunks())} chunks")
+    if name == "gqa_chunk3072":
+        assert plan.decode_chunk == 3072
     log(f"{name}: filling {2 * plan.cache_elems * 2 / 1e9:.2f} GB of rings")
     kc = workloads.device_normal_(torch.empty(plan.cache_elems, dtype=torch.bfloat16,
                                               device="cuda"), 81)
