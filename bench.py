@@ -41,7 +41,8 @@ sys.path.insert(0, ROOT)
 METRIC = ("decode attn tokens/s + HBM GB/s % peak; prefill TFLOP/s % MFMA peak")
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
-PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "decode_c2_counters.json")
+DECODE_COUNTERS = os.path.join(ROOT, "profiles", "decode_c2_counters.json")
+PREFILL_COUNTERS = os.path.join(ROOT, "profiles", "prefill_c1_counters.json")
 
 
 def log(msg):
@@ -79,15 +80,15 @@ def src_sha(*names):
     return h.hexdigest()[:16]
 
 
-def counter_traffic():
-    """Per-launch HBM bytes of the decode kernel from committed counter runs, or None
-    when the kernel sources changed since the counters were taken."""
+def counter_traffic(path, *sources):
+    """Per-launch HBM bytes of a kernel from committed counter runs, or None when its
+    sources changed since the counters were taken."""
     try:
-        with open(PROFILE_COUNTERS) as f:
+        with open(path) as f:
             c = json.load(f)
     except (OSError, ValueError):
         return None
-    if c.get("src_sha") != src_sha("decode.hip", "moa_device.h"):
+    if c.get("src_sha") != src_sha(*sources):
         return None
     return c.get("traffic_bytes_per_launch")
 
@@ -351,7 +352,7 @@ def main():
                 "bytes_per_step": step_bytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": counter_traffic(),
+                     "traffic": counter_traffic(DECODE_COUNTERS, "decode.hip", "moa_device.h"),
                      "kernel": f"moa_append_decode = decode_kernel<{w.head_dim}, true> + "
                                f"decode_combine_kernel<{w.head_dim}, true>",
                      "algorithmic_bytes_per_launch": kbytes,
@@ -401,7 +402,10 @@ def main():
             "flops": fl,
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                         "traffic": None, "kernel": f"prefill_bf16_kernel<{pw.head_dim}>"},
+                         "traffic": (counter_traffic(PREFILL_COUNTERS, "prefill.hip", "moa_device.h",
+                                                     "moa_internal.h", "moa_abi.cpp")
+                                     if pw.name == "c1_prefill" else None),
+                         "kernel": f"prefill_bf16_kernel<{pw.head_dim}>"},
         }
         if not args.no_dense:
             pd = run_prefill(moa, workloads, torch, args.prefill_workload, args.prefill_iters, 3,
