@@ -93,6 +93,18 @@ def counter_traffic(path, *sources):
     return c.get("traffic_bytes_per_launch")
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), for the CPU-baseline record."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -242,6 +254,7 @@ def cpu_baseline_decode(plan, budget_s):
         if el >= budget_s:
             break
     return {"value": tokens / el, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+            "cpu": cpu_model(), "logical_cpus": os.cpu_count(),
             "sample": f"{tokens} decode tokens (one sequence each, all {plan.n_kv_heads} KV heads, "
                       f"full rings) in {el:.1f} s, float64 numpy"}
 
@@ -266,7 +279,7 @@ def cpu_baseline_prefill(plan, budget_s):
         if el >= budget_s:
             break
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_model(), "logical_cpus": os.cpu_count(),
             "sample": f"{rows_done} random query rows over the heads' spans in {el:.1f} s, "
                       f"float64 numpy"}
 
