@@ -350,6 +350,41 @@ def test_error_message_is_thread_local(moa):
     assert moa.last_error() != ""
 
 
+def test_concurrent_plans_are_independent(moa):
+    """Plans created and destroyed on 8 threads at once (the binding's foreign calls release
+    the GIL) give exactly the tables of the same plans made on one thread."""
+    import threading
+    shapes = [(2, 8, 4, 128, 1000, [0, 64, 300, 0], [0.25, 0.0, 0.0, 1.0], None),
+              (3, 4, 2, 64, 777, [0, 100], [0.5, 0.0], [777, 1, 300]),
+              (16, 64, 8, 128, 65536, *workloads.rules("c4_decode"), None)]
+
+    def tables(shape):
+        b, hq, hkv, d, n, a, be, lens = shape
+        p = moa.Plan(b, hq, hkv, d, n, a, be, seq_len=lens, host_only=True)
+        try:
+            return (p.seq_spans.tolist(), p.ring_offsets.tolist(), p.prefill_items().tolist(),
+                    p.decode_chunks().tolist(), p.decode_chunk, p.workspace_bytes, p.cache_elems)
+        finally:
+            p.close()
+
+    want = [tables(sh) for sh in shapes]
+    errors = []
+
+    def worker(k):
+        try:
+            for i in range(6):
+                j = (k + i) % len(shapes)
+                assert tables(shapes[j]) == want[j], (k, i, j)
+        except Exception as e:   # collected and re-raised on the main thread
+            errors.append(e)
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[0]
+
+
 # ---------------------------------------------------------------------------
 # per-sequence prompt lengths (left-padded ragged batch)
 # ---------------------------------------------------------------------------
