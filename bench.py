@@ -294,6 +294,10 @@ def main():
     ap.add_argument("--prefill-iters", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other workloads' legs (C3 and C4 decode, C4 prefill)")
+    ap.add_argument("--extra-steps", type=int, default=64,
+                    help="timed decode steps of each extra decode leg")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense-cache baseline (every span = N) on the same kernels")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -428,6 +432,31 @@ def main():
                 "tflops": round(prefill_flops(pd["plan"]) / (pd["ms"] / 1e3) / 1e12, 2),
                 "moa_speedup": round(pd["ms"] / pres["ms"], 3)}
             log(f"dense prefill: {pd['ms']:.3f} ms, MoA speedup {pd['ms'] / pres['ms']:.2f}x")
+
+    if not args.no_extra:
+        # the other workloads, measured the same way (not the headline): fused decode steps,
+        # and the 64-head 64k GQA prompt
+        other = {}
+        for name in ("c3_decode", "c4_decode"):
+            r = run_decode(moa, workloads, torch, name, args.extra_steps, 8)
+            p, wx = r["plan"], r["w"]
+            ms = r["fused"]["elapsed_ms"] / args.extra_steps
+            gbps = (decode_kernel_bytes(p) + append_bytes(p)) / (r["fused"]["decode_ms"] / 1e3) / 1e9
+            other[name] = {"workload": f"{wx.name}: {wx.title}", "steps": args.extra_steps,
+                           "ms_per_step": round(ms, 4),
+                           "tokens_per_s": round(wx.batch / (ms / 1e3), 1),
+                           "kernel_GBps": round(gbps, 1),
+                           "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+                           "decode_chunk": p.decode_chunk}
+            log(f"{name}: {ms:.4f} ms/step, {gbps:.0f} GB/s ({gbps / HBM_PEAK_GBPS:.1%} of peak)")
+        r = run_prefill(moa, workloads, torch, "c4_prefill", 10, 2)
+        tf4 = prefill_flops(r["plan"]) / (r["ms"] / 1e3) / 1e12
+        other["c4_prefill"] = {"workload": f"{r['w'].name}: {r['w'].title}",
+                               "ms": round(r["ms"], 3), "tflops": round(tf4, 1),
+                               "mfma_frac": round(tf4 / MFMA_BF16_PEAK_TFLOPS, 4),
+                               "fused_prefill_handoff_ms": round(r["fused_ms"], 3)}
+        log(f"c4_prefill: {r['ms']:.2f} ms, {tf4:.0f} TFLOP/s ({tf4 / MFMA_BF16_PEAK_TFLOPS:.1%})")
+        line["other_workloads"] = other
 
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
