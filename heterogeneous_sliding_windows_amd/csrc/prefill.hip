@@ -146,26 +146,26 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
   const int iw0 = qt * BM + wave * 32;  // first query row of this wave
   const int my_q = iw0 + l32;
 
-  // Q pre-scaled by log2(e)/sqrt(D): the scores come out in the exp2 domain
+  // Q goes to the matrix cores as stored: the scores come out raw (fp32), and
+  // log2(e)/sqrt(D) is applied in fp32 before each exponential.  Scaling Q in
+  // bf16 first would round every score by up to 2^-9 of its size, which at
+  // large logits moves the weights by far more than bf16 output rounding.
   bf16x8 qop[KS];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    const bf16x8 x = my_q < N ? ld16(qb + (int64_t)my_q * D + 16 * s + 8 * half) : zero_bf16x8();
-    float f[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = (float)x[e] * scale_log2;
-    qop[s] = to_bf16x8(f);
-  }
+  for (int s = 0; s < KS; ++s)
+    qop[s] = my_q < N ? ld16(qb + (int64_t)my_q * D + 16 * s + 8 * half) : zero_bf16x8();
+  // the lazy-rescale threshold, 8 in the exp2 domain, in raw score units
+  const float thr = 8.f / scale_log2;
 
   floatx16 acc[OT];
 #pragma unroll
   for (int t = 0; t < OT; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
-  // m_run: the row's running max (exp2 domain), -inf before its first kept
+  // m_run: the row's running max (raw score), -inf before its first kept
   // key.  m_ref: the reference the scores are taken against (m_run once set,
   // 0 before); -m_ref seeds the Q.K accumulators, so the matrix cores return
-  // score - m_ref, the exp2 argument itself.
+  // score - m_ref, which times scale_log2 is the exp2 argument.
   float m_run = -INFINITY, m_ref = 0.f;
   float l_a = 0.f, l_b = 0.f;   // row sum, two partial chains
   floatx16 minit;
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      // st[t][r] is score - m_ref of query my_q and key
+      // st[t][r] is raw score - m_ref of query my_q and key
       // j0 + 32t + 16(r>>3) + 8half + (r&7)
       if (!full) {
 #pragma unroll
@@ -291,10 +291,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
       // some row's tile max exceeds it by more than 8 in the exp2 domain, or
       // sets it at the row's first kept key; otherwise p <= 256, harmless in
       // fp32 and bf16.  The final O / l is unchanged.
-      if (__ballot(mx > 8.f || (m_run == -INFINITY && mx != -INFINITY))) {
+      if (__ballot(mx > thr || (m_run == -INFINITY && mx != -INFINITY))) {
         const float m_new = fmaxf(m_run, mx == -INFINITY ? -INFINITY : m_ref + mx);
         const bool set = m_new != -INFINITY;   // else: no kept key yet, nothing moves
-        const float alpha = set ? fast_exp2(m_run - m_new) : 1.f;   // 0 at the first key
+        const float alpha = set ? fast_exp2((m_run - m_new) * scale_log2) : 1.f;   // 0 at the first key
         const float delta = set ? m_new - m_ref : 0.f;
         if (set) {
           m_run = m_new;
@@ -318,7 +318,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) p[t][r] = fast_exp2(st[t][r]);
+        for (int r = 0; r < 16; ++r) p[t][r] = fast_exp2(st[t][r] * scale_log2);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const bf16x8 pop = to_bf16x8(&p[j >> 1][8 * (j & 1)]);
