@@ -35,9 +35,11 @@
 //    t is computed (one wait and one barrier a tile);
 //  * masks are evaluated only on tiles a wave's rows do not fully keep, and a
 //    wave skips tiles none of its rows keep;
-//  * online softmax in fp32 with exp2 and the 1/sqrt(D)*log2(e) scale folded;
-//    O and the row sum are rescaled only when a row's max grows by more than
-//    2^8 (exp2 domain), which most tiles after the first never trigger.
+//  * online softmax in fp32 with exp2: the scores leave the matrix cores raw
+//    (fp32) and 1/sqrt(D)*log2(e) is applied in fp32 before each
+//    exponential; O and the row sum are rescaled only when a row's max grows
+//    by more than 8 in the exp2 domain (a factor of 2^8), which most tiles
+//    after the first never trigger.
 //
 // f32 kernel (the float32 dtype): 2 threads per query row, each owning half
 // of the head dimension; K/V tiles in LDS; plain FMA arithmetic.
