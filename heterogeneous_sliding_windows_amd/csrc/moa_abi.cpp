@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -178,6 +179,25 @@ void build_prefill_items(moa_plan* p) {
       depth = std::max(depth, r.n);
     }
     k0 += (size_t)depth;
+  }
+  // The tail of each XCD's queue, longest units first (stable: equal tile
+  // counts keep their queue order).
+  for (int x = 0; x < 8; ++x) {
+    std::vector<size_t> pos;   // XCD x's entries that hold a unit, in queue order
+    for (size_t k = 0; k < rounds; ++k)
+      if (p->prefill_items[(8 * k + x) * 4] >= 0) pos.push_back(8 * k + x);
+    const size_t t0 = pos.size() > moa::kPrefillTailUnits ? pos.size() - moa::kPrefillTailUnits : 0;
+    std::vector<std::array<int32_t, 4>> tail;
+    for (size_t i = t0; i < pos.size(); ++i) {
+      const int32_t* e = &p->prefill_items[pos[i] * 4];
+      tail.push_back({e[0], e[1], e[2], e[3]});
+    }
+    std::stable_sort(tail.begin(), tail.end(),
+                     [](const std::array<int32_t, 4>& a, const std::array<int32_t, 4>& b) {
+                       return a[3] - a[2] > b[3] - b[2];
+                     });
+    for (size_t i = t0; i < pos.size(); ++i)
+      std::copy(tail[i - t0].begin(), tail[i - t0].end(), &p->prefill_items[pos[i] * 4]);
   }
   p->prefill_seq_grid = p->ragged ? 0 : (int64_t)rounds * 8;
   p->n_prefill_units = (int64_t)units.size() * (p->ragged ? 1 : p->B);

@@ -21,6 +21,10 @@ constexpr int kPrefillBN = 64;
 // three tiles' time).
 constexpr int kPrefillRun = 16;
 constexpr int kPrefillUnitOverhead = 3;
+// The last kPrefillTailUnits units of each XCD's queue (four rounds of its
+// 64 workgroup slots) run in descending tile count, so that the launch ends
+// on its shortest units instead of on the long first units of the last runs.
+constexpr size_t kPrefillTailUnits = 256;
 // Decode chunk (slots of one head's ring per workgroup) for ungrouped heads.
 constexpr int kDecodeChunk = 1024;
 // A chunk of a KV group publishes G partial rows, and those writes, mixed

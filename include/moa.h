@@ -187,7 +187,10 @@ int64_t moa_max_batch(const moa_problem* problem, uint64_t budget_bytes);
  * order; groups of 8 consecutive runs go one run per XCD, XCD j for the j-th
  * run of an even group and 7 - j of an odd one; XCD x's k-th unit runs in
  * workgroup 8k + x, and a group spans as many rounds of 8 workgroups as its
- * longest run.  Workgroup numbers missing from the list are padding.  A plan
+ * longest run; then the last 256 units of each XCD's queue are reordered by
+ * tile count, most first (a stable sort, so equal counts keep their order),
+ * into the same workgroups.  Workgroup numbers missing from the list are
+ * padding.  A plan
  * without per-sequence lengths schedules sequence 0's units this way (T
  * entries, padding included, a multiple of 8) and runs that table once per
  * sequence: sequence b's unit at entry e runs in workgroup b*T + e.

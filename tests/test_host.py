@@ -107,8 +107,9 @@ def _schedule_of(items):
     """Workgroup order rebuilt from the stated rule: runs of up to 16 consecutive query tiles
     of one (b, h_q) from the last tile down; runs longest first (tiles + 3 per unit; ties in
     (b, h_q, run) order); groups of 8 runs, one per XCD in snake order; XCD x's k-th unit in
-    workgroup 8k + x, a group as deep as its longest run.  Returns ({unit: wg}, table length,
-    XCD loads, the costliest run)."""
+    workgroup 8k + x, a group as deep as its longest run; the last 256 units of each XCD's
+    queue then take its last 256 unit workgroups in descending tile count (stable).  Returns
+    ({unit: wg}, table length, XCD loads, the costliest run)."""
     key = {tuple(r[:3]): r for r in items}
     tiles = {}
     for b, hq, qt in key:
@@ -129,6 +130,10 @@ def _schedule_of(items):
             wg.update({u: 8 * (k0 + i) + x for i, u in enumerate(run)})
             load[x] += cost
         k0 += max(len(r[2]) for r in group)
+    for x in range(8):
+        queue = sorted((w, u) for u, w in wg.items() if w % 8 == x)[-256:]
+        by_tiles = sorted((u for _, u in queue), key=lambda u: -(key[u][4] - key[u][3] + 1))
+        wg.update({u: w for (w, _), u in zip(queue, by_tiles)})
     return wg, 8 * k0, load, max(r[0] for r in runs)
 
 
