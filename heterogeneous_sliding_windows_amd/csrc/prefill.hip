@@ -33,6 +33,10 @@
 //    two transposed LDS reads (ds_read_b64_tr_b16);
 //  * LDS tiles are double-buffered: tile t+1's loads are issued before tile
 //    t is computed (one wait and one barrier a tile);
+//  * Q and O go through LDS too: the unit's Q rows arrive by the same
+//    LDS-direct loads (into the second buffers, before the first tile is
+//    computed), and each wave writes its normalised O rows to LDS and stores
+//    them as whole 16-byte chunks, four complete rows per store instruction;
 //  * masks are evaluated only on tiles a wave's rows do not fully keep, and a
 //    wave skips tiles none of its rows keep;
 //  * online softmax in fp32 with exp2: the scores leave the matrix cores raw
@@ -152,10 +156,19 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
   // log2(e)/sqrt(D) is applied in fp32 before each exponential.  Scaling Q in
   // bf16 first would round every score by up to 2^-9 of its size, which at
   // large logits moves the weights by far more than bf16 output rounding.
-  bf16x8 qop[KS];
+  // The unit's 128 Q rows take the same LDS-direct path as the tiles, into
+  // the idle second buffers (rows 0-63 in K's, 64-127 in V's); rows at or
+  // past N read as zero.
+  {
+    const __amdgpu_buffer_rsrc_t qrs = buffer_rsrc(qb, (uint32_t)N * ROWB);
 #pragma unroll
-  for (int s = 0; s < KS; ++s)
-    qop[s] = my_q < N ? ld16(qb + (int64_t)my_q * D + 16 * s + 8 * half) : zero_bf16x8();
+    for (int i = 0; i < NDMA; ++i) {
+      const uint32_t soff = (uint32_t)(qt * BM) * ROWB + i * 64;
+      lds_direct_ld16(qrs, dma_off, soff, (char*)&Ks[1][0] + i * 4096 + wave * 1024);
+      lds_direct_ld16(qrs, dma_off, soff + 64 * ROWB, (char*)&Vs[1][0] + i * 4096 + wave * 1024);
+    }
+  }
+  bf16x8 qop[KS];
   // the lazy-rescale threshold, 8 in the exp2 domain, in raw score units
   const float thr = 8.f / scale_log2;
 
@@ -242,6 +255,13 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
   // tile kt is computed; one wait and one barrier a tile.
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
+  {
+    const char* qs = wave < 2 ? (const char*)&Ks[1][0] : (const char*)&Vs[1][0];
+    const int r = (wave & 1) * 32 + l32;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qop[s] = *reinterpret_cast<const bf16x8*>(qs + tile_off(r, 2 * s + half));
+  }
+  __syncthreads();   // every wave holds its Q before the second buffers take tile kt_lo+1
   for (int kt = kt_lo; kt <= kt_hi; ++kt) {
     const int buf = (kt - kt_lo) & 1;
     if (kt < kt_hi) dma_tile(kt + 1, buf ^ 1);
@@ -354,10 +374,14 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
     __syncthreads();
   }
 
+  // O through LDS: each wave writes its 32 normalised rows into its own part
+  // of the (now idle) K buffers, chunk c of row r at 16 * (c ^ (r mod chunks per row)), and
+  // reads them back as whole 16-byte chunks, so that each store instruction
+  // writes four complete output rows.  Rows at or past N are not stored.
   const float l_run = half_swap_sum(l_a + l_b);
-  if (my_q >= N) return;
   const float inv = 1.f / l_run;
-  bf16* orow = ob + (int64_t)my_q * D;
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  char* ow = (char*)&Ks[0][0] + wave * (32 * D * 2);
 #pragma unroll
   for (int t = 0; t < OT; ++t)
 #pragma unroll
@@ -365,8 +389,15 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
       bf16x4 x;
 #pragma unroll
       for (int c = 0; c < 4; ++c) x[c] = (bf16)(acc[t][4 * a + c] * inv);
-      *reinterpret_cast<bf16x4*>(orow + 32 * t + 8 * a + 4 * half) = x;
+      const int ch = 4 * t + a;              // chunk 32t + 8a .. +7 of the row
+      *reinterpret_cast<bf16x4*>(ow + l32 * (2 * D) + ((ch ^ (l32 % CPR)) << 4) + 8 * half) = x;
     }
+#pragma unroll
+  for (int i = 0; i < 32 * CPR / 64; ++i) {
+    const int r = (i * 64 + lane) / CPR, ch = lane % CPR;
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(ow + r * (2 * D) + ((ch ^ (r % CPR)) << 4));
+    if (iw0 + r < N) st16(ob + (int64_t)(iw0 + r) * D + 8 * ch, x);
+  }
 }
 
 template <int D, bool RING>
