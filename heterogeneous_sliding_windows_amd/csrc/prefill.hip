@@ -33,10 +33,9 @@
 //    two transposed LDS reads (ds_read_b64_tr_b16);
 //  * LDS tiles are double-buffered: tile t+1's loads are issued before tile
 //    t is computed (one wait and one barrier a tile);
-//  * Q and O go through LDS too: the unit's Q rows arrive by the same
-//    LDS-direct loads (into the second buffers, before the first tile is
-//    computed), and each wave writes its normalised O rows to LDS and stores
-//    them as whole 16-byte chunks, four complete rows per store instruction;
+//  * O goes through LDS: each wave writes its normalised rows to LDS and
+//    stores them as whole 16-byte chunks, four complete rows per store
+//    instruction;
 //  * masks are evaluated only on tiles a wave's rows do not fully keep, and a
 //    wave skips tiles none of its rows keep;
 //  * online softmax in fp32 with exp2: the scores leave the matrix cores raw
@@ -156,19 +155,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
   // log2(e)/sqrt(D) is applied in fp32 before each exponential.  Scaling Q in
   // bf16 first would round every score by up to 2^-9 of its size, which at
   // large logits moves the weights by far more than bf16 output rounding.
-  // The unit's 128 Q rows take the same LDS-direct path as the tiles, into
-  // the idle second buffers (rows 0-63 in K's, 64-127 in V's); rows at or
-  // past N read as zero.
-  {
-    const __amdgpu_buffer_rsrc_t qrs = buffer_rsrc(qb, (uint32_t)N * ROWB);
-#pragma unroll
-    for (int i = 0; i < NDMA; ++i) {
-      const uint32_t soff = (uint32_t)(qt * BM) * ROWB + i * 64;
-      lds_direct_ld16(qrs, dma_off, soff, (char*)&Ks[1][0] + i * 4096 + wave * 1024);
-      lds_direct_ld16(qrs, dma_off, soff + 64 * ROWB, (char*)&Vs[1][0] + i * 4096 + wave * 1024);
-    }
-  }
   bf16x8 qop[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+    qop[s] = my_q < N ? ld16(qb + (int64_t)my_q * D + 16 * s + 8 * half) : zero_bf16x8();
   // the lazy-rescale threshold, 8 in the exp2 domain, in raw score units
   const float thr = 8.f / scale_log2;
 
@@ -255,13 +245,6 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
   // tile kt is computed; one wait and one barrier a tile.
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
-  {
-    const char* qs = wave < 2 ? (const char*)&Ks[1][0] : (const char*)&Vs[1][0];
-    const int r = (wave & 1) * 32 + l32;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qop[s] = *reinterpret_cast<const bf16x8*>(qs + tile_off(r, 2 * s + half));
-  }
-  __syncthreads();   // every wave holds its Q before the second buffers take tile kt_lo+1
   for (int kt = kt_lo; kt <= kt_hi; ++kt) {
     const int buf = (kt - kt_lo) & 1;
     if (kt < kt_hi) dma_tile(kt + 1, buf ^ 1);
