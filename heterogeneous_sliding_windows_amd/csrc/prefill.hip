@@ -53,7 +53,9 @@
 // kt*BN/BM, whose item always streams it; the workgroup of the first query
 // head of each KV group (g = 0) stores the rows of its diagonal tiles that the
 // ring keeps, reading them from LDS.  Every ring row is therefore written
-// once, and K/V are read from HBM once.
+// once, and K/V are read from HBM once.  The diagonal tiles are the unit's
+// last one or two, still in their buffers when the loop ends, so the stores
+// follow the loop and the loop itself is the plain kernel's.
 
 #include "moa_device.h"
 #include "moa_internal.h"
@@ -248,7 +250,6 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
   for (int kt = kt_lo; kt <= kt_hi; ++kt) {
     const int buf = (kt - kt_lo) & 1;
     if (kt < kt_hi) dma_tile(kt + 1, buf ^ 1);
-    ring_tile(kt, buf);
 
     const int j0 = kt * BN;
     const bool active = iw0 < N && j0 <= iw0 + 31 && j0 + BN - 1 >= iw0 - S + 1;
@@ -361,6 +362,13 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
   // of the (now idle) K buffers, chunk c of row r at 16 * (c ^ (r mod chunks per row)), and
   // reads them back as whole 16-byte chunks, so that each store instruction
   // writes four complete output rows.  Rows at or past N are not stored.
+  if constexpr (RING) {
+    // The ring keeps rows of the unit's diagonal key tiles (2 qt and 2 qt + 1),
+    // the loop's last one or two tiles, which are still in their buffers.
+    if (kt_hi - 1 >= kt_lo) ring_tile(kt_hi - 1, (kt_hi - 1 - kt_lo) & 1);
+    ring_tile(kt_hi, (kt_hi - kt_lo) & 1);
+    __syncthreads();   // before O is staged in the K buffers
+  }
   const float l_run = half_swap_sum(l_a + l_b);
   const float inv = 1.f / l_run;
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
