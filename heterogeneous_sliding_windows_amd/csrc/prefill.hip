@@ -358,10 +358,6 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
     __syncthreads();
   }
 
-  // O through LDS: each wave writes its 32 normalised rows into its own part
-  // of the (now idle) K buffers, chunk c of row r at 16 * (c ^ (r mod chunks per row)), and
-  // reads them back as whole 16-byte chunks, so that each store instruction
-  // writes four complete output rows.  Rows at or past N are not stored.
   if constexpr (RING) {
     // The ring keeps rows of the unit's diagonal key tiles (2 qt and 2 qt + 1),
     // the loop's last one or two tiles, which are still in their buffers.
@@ -369,6 +365,12 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
     ring_tile(kt_hi, (kt_hi - kt_lo) & 1);
     __syncthreads();   // before O is staged in the K buffers
   }
+
+  // O through LDS: each wave writes its 32 normalised rows into its own part
+  // of the (now idle) K buffers, chunk c of row r at byte
+  // 16 * (c ^ (r mod chunks per row)), and reads them back as whole 16-byte
+  // chunks, so that each store instruction writes four complete output rows.
+  // Rows at or past N are not stored.
   const float l_run = half_swap_sum(l_a + l_b);
   const float inv = 1.f / l_run;
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
