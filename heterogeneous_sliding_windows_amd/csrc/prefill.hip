@@ -316,11 +316,6 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
         for (int r = 0; r < 16; ++r) minit[r] = -m_ref;
       }
       float p[2][16];
-      // Raised wave priority while this wave issues the exponentials and the
-      // P.V products: its matrix ops go out first, and the SIMD's other wave
-      // (another workgroup's) takes the issue slots left between them
-      // (measured 2-3 % faster than default priority on both prompt sizes).
-      __builtin_amdgcn_s_setprio(2);
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -352,7 +347,6 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
-      __builtin_amdgcn_s_setprio(0);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): tile kt+1 is in LDS
     __syncthreads();
