@@ -42,6 +42,7 @@ from .moa_oracle import (  # noqa: F401
     band_mask,
     attention_probs,
     prefill,
+    prefill_row_block,
     prefill_rows,
     decode_step,
     decode,

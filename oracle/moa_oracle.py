@@ -200,6 +200,31 @@ def prefill_rows(q_rows, k, v, s, rows, scale=None):
     return out
 
 
+def prefill_row_block(q_rows, k, v, s, i0, scale=None):
+    """Output rows i0 .. i0 + R - 1 of one head (R = len(q_rows)), as a block.
+
+    The same definition as attention_probs, restricted to the keys any of these
+    rows can keep: keys max(0, i0 - s + 1) .. i0 + R - 1, with the explicit
+    band mask of each row over them (blog digest section 2.1; project page
+    "Finding 2" figure).  k, v [N, D].  Returns float64 [R, D].
+    """
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    r, d = q_rows.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    j0 = max(0, i0 - s + 1)
+    j1 = i0 + r
+    kk = np.asarray(k[j0:j1], dtype=np.float64)
+    vv = np.asarray(v[j0:j1], dtype=np.float64)
+    i = np.arange(i0, j1)[:, None]
+    j = np.arange(j0, j1)[None, :]
+    z = (q_rows @ kk.T) * scale
+    z = np.where((j <= i) & (j >= i - s + 1), z, -np.inf)
+    z = z - z.max(axis=1, keepdims=True)
+    e = np.exp(z)
+    return (e / e.sum(axis=1, keepdims=True)) @ vv
+
+
 # ---------------------------------------------------------------------------
 # Decode over a fixed-size window
 # ---------------------------------------------------------------------------

@@ -109,8 +109,32 @@ def test_c1_prefill_full_size_sampled_rows(moa):
     log(f"c1 worst sampled err {worst:.3e}")
 
 
-def test_c4_prefill_full_size_sampled_rows(moa):
-    """Llama3-70B-shaped GQA prefill (N=65536) on device-generated inputs, sampled rows."""
+def test_c1_prefill_full_size_every_row(moa):
+    """Vicuna-7B-shaped prefill checked in full: every row of every head against the
+    oracle's explicit-mask prefill, one head at a time (an 8192 x 8192 float64 score matrix
+    per head)."""
+    w = workloads.WORKLOADS["c1_prefill"]
+    alpha, beta = workloads.rules("c1_prefill")
+    plan = moa.Plan(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, alpha, beta)
+    q, k, v = workloads.prefill_inputs(w.batch, w.n_q_heads, w.n_kv_heads, w.n_prompt,
+                                       w.head_dim, "bf16", w.data_seed)
+    log("prefill c1 full size, every row")
+    o = _run_prefill(moa, plan, q, k, v).cpu()
+    worst = 0.0
+    for h in range(w.n_q_heads):
+        s = int(plan.spans[h])
+        want = oracle.prefill(f64(q[:, h:h + 1]), f64(k[:, h:h + 1]), f64(v[:, h:h + 1]), [s])
+        err = max_err(f64(o[:, h:h + 1]), want)
+        worst = max(worst, err)
+        assert err <= TOL["bf16"], (h, s, err)
+    log(f"c1 every row: worst err {worst:.3e}")
+
+
+def test_c4_prefill_full_size_row_blocks(moa):
+    """Llama3-70B-shaped GQA prefill (N=65536) on device-generated inputs.  Every query head
+    is checked on 512 rows: four blocks of 128 consecutive rows (the first rows, the rows
+    around S_h, a seeded random block and the last rows) against the oracle's
+    explicit-mask row block."""
     w = workloads.WORKLOADS["c4_prefill"]
     alpha, beta = workloads.rules("c4_prefill")
     plan = moa.Plan(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, alpha, beta)
@@ -123,15 +147,17 @@ def test_c4_prefill_full_size_sampled_rows(moa):
     log("prefill c4 full size")
     plan.prefill(q, k, v, o)
     torch.cuda.synchronize()
-    g = w.n_q_heads // w.n_kv_heads
+    n, g, blk = w.n_prompt, w.n_q_heads // w.n_kv_heads, 128
+    rng = np.random.Generator(np.random.PCG64(204))
     worst = 0.0
     for hk in range(w.n_kv_heads):
         s = int(plan.spans[hk])
         kh, vh = f64(k[0, hk]), f64(v[0, hk])
-        for hq in (hk * g, hk * g + g - 1):
-            rows = sample_rows(w.n_prompt, s, 10, 200 + hq)
-            want = oracle.prefill_rows(f64(q[0, hq, rows]), kh, vh, s, rows)
-            err = max_err(f64(o[0, hq, rows]), want)
-            worst = max(worst, err)
-            assert err <= TOL["bf16"], (hq, s, err)
-    log(f"c4 prefill worst sampled err {worst:.3e}")
+        for hq in range(hk * g, hk * g + g):
+            starts = [0, min(max(0, s - blk // 2), n - blk), int(rng.integers(0, n - blk)), n - blk]
+            for i0 in starts:
+                want = oracle.prefill_row_block(f64(q[0, hq, i0:i0 + blk]), kh, vh, s, i0)
+                err = max_err(f64(o[0, hq, i0:i0 + blk]), want)
+                worst = max(worst, err)
+                assert err <= TOL["bf16"], (hq, s, i0, err)
+    log(f"c4 prefill worst err over 512 rows of every head {worst:.3e}")

@@ -269,6 +269,9 @@ def check_bruteforce_tiny():
         rows = [0, 3, 12]
         got_rows = oracle.prefill_rows(q[0, 0, rows], k[0, 0], v[0, 0], s, rows)
         np.testing.assert_allclose(got_rows, want[rows], rtol=0, atol=1e-12)
+        for i0, r in ((0, 4), (3, 5), (7, 6), (12, 1), (0, 13)):
+            got_blk = oracle.prefill_row_block(q[0, 0, i0:i0 + r], k[0, 0], v[0, 0], s, i0)
+            np.testing.assert_allclose(got_blk, want[i0:i0 + r], rtol=0, atol=1e-12)
 
 
 def test_bruteforce_tiny():
@@ -387,6 +390,22 @@ def _mut_swap_kv_prefill(q, k, v, span, scale=None):
 
 _orig_prefill = moa_oracle.prefill
 
+
+def _mut_block_keys_late(q_rows, k, v, s, i0, scale=None):
+    """Keys taken from i0 - s + 2 on: the oldest kept key of the block's first row dropped."""
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    r, d = q_rows.shape
+    j0 = max(0, i0 - s + 2)
+    out = np.empty((r, d))
+    for a in range(r):
+        i = i0 + a
+        lo = max(j0, i - s + 1)
+        kk, vv = np.asarray(k[lo:i + 1], dtype=np.float64), np.asarray(v[lo:i + 1], dtype=np.float64)
+        z = kk @ q_rows[a] / math.sqrt(d)
+        e = np.exp(z - z.max())
+        out[a] = (e / e.sum()) @ vv
+    return out
+
 MUTATIONS = {
     "window_wide": ("band_mask", _mut_window_wide),
     "window_narrow": ("band_mask", _mut_window_narrow),
@@ -397,6 +416,7 @@ MUTATIONS = {
     "decode_window_wide": ("decode_step", _mut_decode_step_wide),
     "no_scale": ("attention_probs", _mut_no_scale),
     "swap_kv": ("prefill", _mut_swap_kv_prefill),
+    "block_keys_late": ("prefill_row_block", _mut_block_keys_late),
 }
 
 
