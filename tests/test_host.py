@@ -33,6 +33,26 @@ def test_exports_every_declared_symbol(moa):
     assert "gfx950" in moa.version()
 
 
+def test_binding_fails_loudly_without_the_library(moa, tmp_path):
+    """The package has no fallback: without libmoa.so next to it, importing it raises."""
+    import importlib.util
+    import shutil
+    import sys
+    pkg = tmp_path / "moa_copy"
+    pkg.mkdir()
+    for f in ("__init__.py", "rules.py"):
+        shutil.copy(os.path.join(os.path.dirname(moa.__file__), f), pkg / f)
+    spec = importlib.util.spec_from_file_location("moa_copy", pkg / "__init__.py",
+                                                  submodule_search_locations=[str(pkg)])
+    mod = importlib.util.module_from_spec(spec)
+    sys.modules["moa_copy"] = mod
+    try:
+        with pytest.raises(ImportError, match="is not built"):
+            spec.loader.exec_module(mod)
+    finally:
+        sys.modules.pop("moa_copy", None)
+
+
 def _rule_cases():
     rng = np.random.Generator(np.random.PCG64(5))
     cases = []
