@@ -53,6 +53,9 @@ CASES = [
     (2, 8, 1, 64, 1100, [0], [0.97], 3),
     (1, 1, 1, 128, 5, [0], [0.5], 6),
     (2, 6, 3, 64, 2049, [0, 64, 2000], [1.0, 0.0, 0.0], 3),
+    # rings of exactly one and two 1024-slot chunks
+    (1, 4, 2, 128, 1024, [1024, 0], [0.0, 0.5], 3),
+    (1, 2, 2, 128, 2048, [0, 0], [1.0, 0.5], 3),
 ]
 
 

@@ -50,6 +50,11 @@ CASES = [
     (1, 2, 1, 128, 1, [0], [1.0], "bf16"),
     (1, 2, 2, 128, 130, [64, 0], [0.0, 0.0], "bf16"),
     (5, 4, 2, 128, 700, [0, 300], [0.5, 0.0], "bf16"),
+    # prompt lengths at and just past tile boundaries (64-key tiles, 128-row units)
+    (1, 4, 2, 128, 128, [0, 64], [1.0, 0.0], "bf16"),
+    (1, 2, 2, 64, 64, [0, 1], [1.0, 0.0], "bf16"),
+    (2, 4, 4, 128, 65, [0, 64, 1, 0], [0.5, 0.0, 0.0, 1.0], "bf16"),
+    (1, 4, 2, 128, 256, [128, 0], [0.0, 0.5], "bf16"),
     (2, 4, 2, 64, 333, [0, 200], [0.5, 0.0], "f32"),
     (1, 2, 2, 128, 257, [0, 64], [1.0, 0.0], "f32"),
 ]
