@@ -1,0 +1,91 @@
+"""A property that holds at any size, checked at the full sizes without the oracle.
+
+With q = 0 every kept score is 0, so every kept key has the same weight and each output row is
+the plain mean of V over its window: query i of a head with span S averages value rows
+max(0, i - S + 1) .. i in prefill, and a decode step averages the S slots of its ring after
+the new token's append.  The means are computed here in float64 from cumulative sums (prefill)
+or from the ring contents (decode), so they share nothing with the oracle's softmax.  The
+kernels' weights are then exactly 1 (exp2(0)); what separates them from the mean is float32
+accumulation and the final bf16 rounding, so each output must lie within one bf16 ulp of the
+exact mean (|mean| * 2^-7) plus 1e-4 for the float32 sums.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_util import f64, log, ring_v
+
+pytestmark = pytest.mark.gpu
+
+
+def _ulp_excess(got, want):
+    """Largest amount by which |got - want| exceeds one bf16 ulp of want plus 1e-4 (<= 0: ok),
+    and the largest |got - want|."""
+    diff = np.abs(np.asarray(got, dtype=np.float64) - want)
+    return float(np.max(diff - (np.abs(want) * 2.0 ** -7 + 1e-4))), float(np.max(diff))
+
+
+def _window_means(v, s):
+    """[N, D] float64 -> row i: mean of v[max(0, i - s + 1) .. i]."""
+    n = v.shape[0]
+    c = np.concatenate([np.zeros((1, v.shape[1])), np.cumsum(v, axis=0)])
+    i = np.arange(n)
+    lo = np.maximum(0, i - s + 1)
+    return (c[i + 1] - c[lo]) / (i + 1 - lo)[:, None]
+
+
+@pytest.mark.parametrize("name", ["c1_prefill", "c4_prefill"])
+def test_prefill_zero_query_is_window_mean(moa, name):
+    w = workloads.WORKLOADS[name]
+    alpha, beta = workloads.rules(name)
+    plan = moa.Plan(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, alpha, beta)
+    n, g = w.n_prompt, w.n_q_heads // w.n_kv_heads
+    q = torch.zeros(w.batch, w.n_q_heads, n, w.head_dim, dtype=torch.bfloat16, device="cuda")
+    shp_kv = (w.batch, w.n_kv_heads, n, w.head_dim)
+    k = workloads.device_normal_(torch.empty(shp_kv, dtype=torch.bfloat16, device="cuda"), 61)
+    v = workloads.device_normal_(torch.empty(shp_kv, dtype=torch.bfloat16, device="cuda"), 62)
+    o = torch.empty_like(q)
+    log(f"{name}: q = 0, every row of every head against the window mean of v")
+    plan.prefill(q, k, v, o)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for hk in range(w.n_kv_heads):
+        want = _window_means(f64(v[0, hk]), int(plan.spans[hk]))
+        for hq in range(hk * g, (hk + 1) * g):
+            excess, err = _ulp_excess(f64(o[0, hq]), want)
+            worst = max(worst, err)
+            assert excess <= 0, (name, hq, int(plan.spans[hk]), err)
+    log(f"{name}: worst abs err {worst:.3e}, every element within one bf16 ulp")
+
+
+@pytest.mark.parametrize("name", ["c2_decode", "c4_decode"])
+def test_append_decode_zero_query_is_ring_mean(moa, name):
+    w = workloads.WORKLOADS[name]
+    alpha, beta = workloads.rules(name)
+    plan = moa.Plan(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, alpha, beta)
+    g = w.n_q_heads // w.n_kv_heads
+    kc = workloads.device_normal_(torch.empty(plan.cache_elems, dtype=torch.bfloat16,
+                                              device="cuda"), 63)
+    vc = workloads.device_normal_(torch.empty(plan.cache_elems, dtype=torch.bfloat16,
+                                              device="cuda"), 64)
+    ws = plan.new_workspace()
+    q = torch.zeros(w.batch, w.n_q_heads, w.head_dim, dtype=torch.bfloat16, device="cuda")
+    kn = workloads.device_normal_(torch.empty(w.batch, w.n_kv_heads, w.head_dim,
+                                              dtype=torch.bfloat16, device="cuda"), 65)
+    vn = workloads.device_normal_(torch.empty(w.batch, w.n_kv_heads, w.head_dim,
+                                              dtype=torch.bfloat16, device="cuda"), 66)
+    o = torch.empty_like(q)
+    log(f"{name}: q = 0, every (b, h) against the mean of its ring after the append")
+    plan.append_decode(q, kc, vc, kn, vn, w.n_prompt, o, ws)
+    torch.cuda.synchronize()
+    vc_h, o_h = vc.cpu(), f64(o)
+    worst = 0.0
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            want = f64(ring_v(vc_h, plan, b, h)).mean(axis=0)
+            excess, err = _ulp_excess(o_h[b, h * g:(h + 1) * g], want[None, :])
+            worst = max(worst, err)
+            assert excess <= 0, (name, b, h, int(plan.spans[h]), err)
+    log(f"{name}: worst abs err {worst:.3e}, every element within one bf16 ulp")
