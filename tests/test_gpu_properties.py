@@ -1,4 +1,6 @@
-"""A property that holds at any size, checked at the full sizes without the oracle.
+"""Properties checked without the oracle.
+
+The window mean (full sizes):
 
 With q = 0 every kept score is 0, so every kept key has the same weight and each output row is
 the plain mean of V over its window: query i of a head with span S averages value rows
@@ -8,6 +10,8 @@ or from the ring contents (decode), so they share nothing with the oracle's soft
 kernels' weights are then exactly 1 (exp2(0)); what separates them from the mean is float32
 accumulation and the final bf16 rounding, so each output must lie within one bf16 ulp of the
 exact mean (|mean| * 2^-7) plus 1e-4 for the float32 sums.
+
+Grouped-query heads: a grouped plan equals an ungrouped one on repeated K/V.
 """
 
 import numpy as np
@@ -89,3 +93,38 @@ def test_append_decode_zero_query_is_ring_mean(moa, name):
             worst = max(worst, err)
             assert excess <= 0, (name, b, h, int(plan.spans[h]), err)
     log(f"{name}: worst abs err {worst:.3e}, every element within one bf16 ulp")
+
+
+def test_gqa_equals_repeated_kv(moa):
+    """Query head h of a grouped plan reads KV head h // G: the same as an ungrouped plan on
+    K/V repeated G times with the spans repeated.  Prefill does the same arithmetic per unit
+    either way (bit-identical); decode splits the rings into different chunks (within 2e-3)."""
+    bsz, hq, hkv, d, n = 2, 16, 2, 128, 2100
+    alpha, beta = [0, 700], [0.5, 0.0]
+    g = hq // hkv
+    grouped = moa.Plan(bsz, hq, hkv, d, n, alpha, beta)
+    flat = moa.Plan(bsz, hq, hq, d, n, [a for a in alpha for _ in range(g)],
+                    [b for b in beta for _ in range(g)])
+    assert [int(s) for s in flat.spans] == [int(s) for s in grouped.spans for _ in range(g)]
+    q, k, v = (x.cuda() for x in workloads.prefill_inputs(bsz, hq, hkv, n, d, "bf16", 6700))
+    krep, vrep = k.repeat_interleave(g, dim=1).contiguous(), v.repeat_interleave(g, dim=1).contiguous()
+    o_g, o_f = torch.empty_like(q), torch.empty_like(q)
+    kc_g, vc_g = grouped.new_cache()
+    kc_f, vc_f = flat.new_cache()
+    grouped.prefill_handoff(q, k, v, o_g, kc_g, vc_g)
+    flat.prefill_handoff(q, krep, vrep, o_f, kc_f, vc_f)
+    qs, ks, vs = (x.cuda() for x in workloads.decode_step_inputs(bsz, hq, hkv, 1, d, "bf16", 6701))
+    od_g = torch.empty(bsz, hq, d, dtype=torch.bfloat16, device="cuda")
+    od_f = torch.empty_like(od_g)
+    grouped.append_decode(qs[0], kc_g, vc_g, ks[0], vs[0], n, od_g, grouped.new_workspace())
+    flat.append_decode(qs[0], kc_f, vc_f, ks[0].repeat_interleave(g, dim=1).contiguous(),
+                       vs[0].repeat_interleave(g, dim=1).contiguous(), n, od_f,
+                       flat.new_workspace())
+    torch.cuda.synchronize()
+    assert torch.equal(o_g, o_f)
+    err = float((od_g.float() - od_f.float()).abs().max())
+    log(f"gqa vs repeated kv: prefill bit-identical, decode max diff {err:.3e} "
+        f"(chunks {grouped.decode_chunk} vs {flat.decode_chunk})")
+    assert err <= 2e-3
+    grouped.close()
+    flat.close()
