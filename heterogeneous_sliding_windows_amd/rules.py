@@ -74,6 +74,30 @@ class RuleSet:
             raise
         return out
 
+    @staticmethod
+    def caches(plans):
+        """Rings of every layer in one K and one V allocation: [(k_cache, v_cache)] per layer.
+
+        A plan's ring pool is one contiguous range, so layer l's rings are a slice of the
+        shared pool.  Each pool is a whole number of 32-slot blocks of D elements, so every
+        slice starts at least 4 KB into the allocation and keeps the rings' alignment.
+        Zero-filled, on the current GPU."""
+        import torch
+        if not plans:
+            return []
+        dt = plans[0]._torch_dtype()
+        if any(p._torch_dtype() != dt for p in plans):
+            raise ValueError("all layers need the same dtype")
+        total = sum(int(p.cache_elems) for p in plans)
+        k = torch.zeros(total, dtype=dt, device="cuda")
+        v = torch.zeros(total, dtype=dt, device="cuda")
+        out, off = [], 0
+        for p in plans:
+            n = int(p.cache_elems)
+            out.append((k[off:off + n], v[off:off + n]))
+            off += n
+        return out
+
     def to_dict(self):
         return {"format": FORMAT, "version": VERSION, "n_kv_heads": self.n_kv_heads,
                 "layers": [{"alpha": [int(x) for x in a], "beta": [float(x) for x in b]}

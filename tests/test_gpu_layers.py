@@ -66,3 +66,72 @@ def test_layers_from_rules_file(moa):
         for p in plans:
             p.close()
     log(f"layers: worst err {worst:.3e}")
+
+
+def test_decode_step_across_layers_in_one_graph(moa):
+    """Three layers' rings in one K and one V allocation (RuleSet.caches), and a decode step
+    of all three layers captured as one HIP graph.  Each of three replays (the rings restored
+    by eager copies in between) equals the eager calls bit for bit."""
+    import heterogeneous_sliding_windows_amd.rules as rules
+    full = rules.load(os.path.join(GOLDEN, "model_rules.json"))
+    rs = rules.RuleSet([(a[:8], b[:8]) for a, b in full.layers[:3]])
+    bsz, hq, hkv, d, n = 2, 16, 8, 64, 1200
+    plans = rs.plans(bsz, hq, d, n)
+    caches = rules.RuleSet.caches(plans)
+    pool_elems = sum(int(p.cache_elems) for p in plans)
+    assert all(kc.data_ptr() - caches[0][0].data_ptr() ==
+               2 * sum(int(p.cache_elems) for p in plans[:i]) for i, (kc, _) in enumerate(caches))
+    try:
+        for layer, (plan, (kc, vc)) in enumerate(zip(plans, caches)):
+            q, k, v = (x.cuda() for x in workloads.prefill_inputs(bsz, hq, hkv, n, d, "bf16",
+                                                                  9700 + layer))
+            plan.prefill_handoff(q, k, v, torch.empty_like(q), kc, vc)
+        steps = [tuple(x.cuda() for x in workloads.decode_step_inputs(bsz, hq, hkv, 1, d, "bf16",
+                                                                      9800 + layer))
+                 for layer in range(len(plans))]
+        ws = [p.new_workspace() for p in plans]
+        torch.cuda.synchronize()
+        k_pre = [kc.clone() for kc, _ in caches]
+        v_pre = [vc.clone() for _, vc in caches]
+
+        def step(outs):
+            for plan, (kc, vc), (qs, ks, vs), w, o in zip(plans, caches, steps, ws, outs):
+                plan.append_decode(qs[0], kc, vc, ks[0], vs[0], n, o, w)
+
+        def restore():
+            for (kc, vc), k0, v0 in zip(caches, k_pre, v_pre):
+                kc.copy_(k0)
+                vc.copy_(v0)
+
+        ref = [torch.empty(bsz, hq, d, dtype=torch.bfloat16, device="cuda") for _ in plans]
+        step(ref)
+        torch.cuda.synchronize()
+        k_ref = [kc.clone() for kc, _ in caches]
+        v_ref = [vc.clone() for _, vc in caches]
+        restore()
+        outs = [torch.empty_like(r) for r in ref]
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(outs)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step(outs)
+        for rep in range(3):
+            restore()
+            for o in outs:
+                o.zero_()
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            for layer in range(len(plans)):
+                assert torch.equal(outs[layer], ref[layer]), (rep, layer)
+                assert torch.equal(caches[layer][0], k_ref[layer]), (rep, layer)
+                assert torch.equal(caches[layer][1], v_ref[layer]), (rep, layer)
+        log(f"layers in one graph: {len(plans)} layers, rings in one pool of "
+            f"{2 * pool_elems * 2 / 1e6:.1f} MB, three replays bit-identical")
+    finally:
+        for p in plans:
+            p.close()
