@@ -116,12 +116,15 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 // LDS-direct buffer load: lane l's 16 bytes at voff + soff of the resource
 // land at LDS byte (lds + 16 l) (one wave fills 1 KB).  Out-of-range reads
 // give zeros.  Not tracked by the compiler's wait counting: the caller waits
-// with vmcnt(0) before the data is read.  The s_nop is the one wait state a
-// write of M0 needs before an LDS-direct load reads it.
+// with vmcnt(0) before the data is read.  The compiler's hazard checks do not
+// look inside assembly, so the block waits for itself: a VALU write of an SGPR
+// (v_readlane reloading a spilled resource word, v_readfirstlane) needs five
+// wait states before a vector memory instruction reads that SGPR, and a write
+// of M0 one before an LDS-direct load uses it; s_nop 4 covers both.
 __device__ __forceinline__ void lds_direct_ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
                                                 uint32_t soff, void* lds) {
   const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :
                : "v"(voff), "s"(r), "s"(soff), "{m0}"(m0)
                : "memory");

@@ -379,6 +379,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
       const int ch = 4 * t + a;              // chunk 32t + 8a .. +7 of the row
       *reinterpret_cast<bf16x4*>(ow + l32 * (2 * D) + ((ch ^ (l32 % CPR)) << 4) + 8 * half) = x;
     }
+  // Each lane reads back chunks that other lanes wrote.  Lanes sharing data
+  // through LDS need a barrier between the writes and the reads; without one
+  // the compiler may move a lane's reads above its writes, which do not alias.
+  __syncthreads();
 #pragma unroll
   for (int i = 0; i < 32 * CPR / 64; ++i) {
     const int r = (i * 64 + lane) / CPR, ch = lane % CPR;
