@@ -92,6 +92,8 @@ APPEND_CASES = [
     (2, 4, 2, 128, 2175, [1088, 1024], [0.0, 0.0], 3),
     # new slot in a later chunk of a multi-chunk ring
     (1, 8, 2, 64, 3100, [2048, 0], [0.0, 0.4], 3),
+    # more steps than either span (64 and 100): every slot rewritten by decode tokens
+    (2, 4, 2, 128, 100, [64, 0], [0.0, 1.0], 150),
 ]
 
 
