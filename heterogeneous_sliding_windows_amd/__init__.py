@@ -242,6 +242,8 @@ class Plan:
             raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
+        if t.data_ptr() % 16:
+            raise ValueError(f"{name} must start at a 16-byte aligned address")
         return ctypes.c_void_p(t.data_ptr())
 
     def cache_shape(self):
@@ -280,8 +282,8 @@ class Plan:
     def _ws(workspace):
         import torch
         if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" \
-                or not workspace.is_contiguous():
-            raise ValueError("workspace must be a contiguous GPU tensor")
+                or not workspace.is_contiguous() or workspace.data_ptr() % 16:
+            raise ValueError("workspace must be a contiguous, 16-byte aligned GPU tensor")
         return ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
 
     def decode(self, q, k_cache, v_cache, pos, o, workspace, stream=None):

@@ -12,6 +12,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <new>
 #include <string>
 #include <vector>
@@ -228,6 +229,15 @@ void build_decode_chunks(moa_plan* p) {
   p->n_chunks = idx;
 }
 
+// Device pointers must be 16-byte aligned (include/moa.h): the kernels move
+// 16-byte vectors through them.  Null entries are skipped (checked elsewhere).
+int check_aligned(const char* who, std::initializer_list<const void*> ptrs) {
+  for (const void* x : ptrs)
+    if (x != nullptr && (reinterpret_cast<uintptr_t>(x) & 15u) != 0)
+      return fail(MOA_EINVAL, "%s: device pointer %p is not 16-byte aligned", who, x);
+  return MOA_OK;
+}
+
 int check_plan(moa_plan_t p, bool need_device) {
   if (!p) return fail(MOA_EINVAL, "plan is NULL");
   if (need_device && p->host_only)
@@ -248,9 +258,11 @@ int set_device(const moa_plan* p) {
 // must be current).
 int check_prefill(moa_plan_t p, const void* q, const void* k, const void* v, const void* o,
                   const char* who) {
-  int st = check_plan(p, true);
+  int st = check_plan(p, false);
   if (st != MOA_OK) return st;
   if (!q || !k || !v || !o) return fail(MOA_EINVAL, "%s: q, k, v and o must not be NULL", who);
+  if ((st = check_aligned(who, {q, k, v, o})) != MOA_OK) return st;
+  if ((st = check_plan(p, true)) != MOA_OK) return st;
   if (p->N * p->D * (p->dtype == MOA_BF16 ? 2 : 4) >= ((int64_t)1 << 31))
     return fail(MOA_EUNSUPPORTED, "%s: one head's K/V (N x head_dim) must stay below 2 GiB", who);
   const uint64_t table = p->prefill_items.size() / 4;
@@ -259,13 +271,16 @@ int check_prefill(moa_plan_t p, const void* q, const void* k, const void* v, con
   return set_device(p);
 }
 
-// Checks shared by moa_decode and moa_append_decode.
+// Checks shared by moa_decode and moa_append_decode (need_ws = false skips
+// the workspace checks).
 int check_decode(moa_plan_t p, const void* q, const void* kc, const void* vc, int64_t pos,
-                 const void* o, const void* ws, size_t ws_bytes, const char* who) {
-  int st = check_plan(p, true);
+                 const void* o, const void* ws, size_t ws_bytes, bool need_ws, const char* who) {
+  int st = check_plan(p, false);
   if (st != MOA_OK) return st;
-  if (!q || !kc || !vc || !o || !ws)
-    return fail(MOA_EINVAL, "%s: q, caches, o and workspace must not be NULL", who);
+  if (!q || !kc || !vc || !o) return fail(MOA_EINVAL, "%s: q, caches and o must not be NULL", who);
+  if (need_ws && !ws) return fail(MOA_EINVAL, "%s: workspace must not be NULL", who);
+  if ((st = check_aligned(who, {q, kc, vc, o, need_ws ? ws : nullptr})) != MOA_OK) return st;
+  if ((st = check_plan(p, true)) != MOA_OK) return st;
   if (pos < p->N)
     return fail(MOA_EINVAL, "%s: pos (%lld) must be >= the prompt length %lld", who,
                 (long long)pos, (long long)p->N);
@@ -280,7 +295,7 @@ int check_decode(moa_plan_t p, const void* q, const void* kc, const void* vc, in
                   p->D);
   }
   const size_t need = moa::decode_ws_bytes(*p);
-  if (ws_bytes < need)
+  if (need_ws && ws_bytes < need)
     return fail(MOA_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", who, ws_bytes, need);
   return set_device(p);
 }
@@ -477,15 +492,31 @@ int64_t moa_max_batch(const moa_problem* pr, uint64_t budget_bytes) {
     for (const int32_t sp : span) n += (uint64_t)((sp + c - 1) / c);
     return n;
   };
-  // the workspace of batch b uses the chunk size a plan of batch b would take
-  auto bytes = [&](uint64_t b) {
-    const int c = moa::decode_chunk_for(G, [&](int cc) { return (int64_t)(b * per_seq(cc)); });
-    uint64_t w = (b * per_seq(c) * row + 255) & ~(uint64_t)255;
-    return b * cache + (w < 256 ? 256 : w);
+  // bytes(b): both pools of b sequences plus the workspace a plan of batch b
+  // would take; UINT64_MAX when that overflows (it cannot fit any budget)
+  auto bytes = [&](uint64_t b) -> uint64_t {
+    const int c = moa::decode_chunk_for(G, [&](int cc) {
+      uint64_t n;
+      return __builtin_mul_overflow(b, per_seq(cc), &n) || n > (uint64_t)INT64_MAX
+                 ? INT64_MAX : (int64_t)n;
+    });
+    uint64_t pools, chunks, ws;
+    if (__builtin_mul_overflow(b, cache, &pools) ||
+        __builtin_mul_overflow(b, per_seq(c), &chunks) ||
+        __builtin_mul_overflow(chunks, row, &ws) || ws > UINT64_MAX - 511)
+      return UINT64_MAX;
+    ws = (ws + 255) & ~(uint64_t)255;
+    if (ws < 256) ws = 256;
+    uint64_t total;
+    if (__builtin_add_overflow(pools, ws, &total)) return UINT64_MAX;
+    return total;
   };
+  // a plan's batch is int32, so the answer is capped there
+  const uint64_t kMaxB = (uint64_t)INT32_MAX;
   uint64_t b = budget_bytes / (cache + per_seq(moa::kDecodeChunk) * row);
+  if (b > kMaxB) b = kMaxB;
   while (b > 0 && bytes(b) > budget_bytes) --b;
-  while (bytes(b + 1) <= budget_bytes) ++b;
+  while (b < kMaxB && bytes(b + 1) <= budget_bytes) ++b;
   return (int64_t)b;
 }
 
@@ -543,9 +574,10 @@ int moa_prefill(moa_plan_t p, const void* q, const void* k, const void* v, void*
 
 int moa_prefill_handoff(moa_plan_t p, const void* q, const void* k, const void* v, void* o,
                         void* kc, void* vc, void* stream) {
-  int st = check_prefill(p, q, k, v, o, "moa_prefill_handoff");
-  if (st != MOA_OK) return st;
   if (!kc || !vc) return fail(MOA_EINVAL, "moa_prefill_handoff: k_cache and v_cache must not be NULL");
+  int st = check_aligned("moa_prefill_handoff", {kc, vc});
+  if (st != MOA_OK) return st;
+  if ((st = check_prefill(p, q, k, v, o, "moa_prefill_handoff")) != MOA_OK) return st;
   hipError_t e = moa::launch_prefill(*p, q, k, v, o, kc, vc, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "prefill_handoff launch");
   return MOA_OK;
@@ -553,10 +585,12 @@ int moa_prefill_handoff(moa_plan_t p, const void* q, const void* k, const void* 
 
 int moa_kv_append(moa_plan_t p, void* kc, void* vc, const void* kn, const void* vn, int64_t pos0,
                   int64_t n_new, void* stream) {
-  int st = check_plan(p, true);
+  int st = check_plan(p, false);
   if (st != MOA_OK) return st;
   if (!kc || !vc || !kn || !vn)
     return fail(MOA_EINVAL, "moa_kv_append: caches and new rows must not be NULL");
+  if ((st = check_aligned("moa_kv_append", {kc, vc, kn, vn})) != MOA_OK) return st;
+  if ((st = check_plan(p, true)) != MOA_OK) return st;
   if (pos0 < 0) return fail(MOA_EINVAL, "moa_kv_append: pos0 must be >= 0 (got %lld)", (long long)pos0);
   if (n_new < 1) return fail(MOA_EINVAL, "moa_kv_append: n_new must be >= 1 (got %lld)", (long long)n_new);
   if (n_new >= kMaxN || pos0 > ((int64_t)1 << 62) - n_new)
@@ -569,7 +603,7 @@ int moa_kv_append(moa_plan_t p, void* kc, void* vc, const void* kn, const void* 
 
 int moa_decode(moa_plan_t p, const void* q, const void* kc, const void* vc, int64_t pos, void* o,
                void* ws, size_t ws_bytes, void* stream) {
-  int st = check_decode(p, q, kc, vc, pos, o, ws, ws_bytes, "moa_decode");
+  int st = check_decode(p, q, kc, vc, pos, o, ws, ws_bytes, true, "moa_decode");
   if (st != MOA_OK) return st;
   hipError_t e = moa::launch_decode_bf16(*p, q, kc, vc, o, ws, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
@@ -579,9 +613,12 @@ int moa_decode(moa_plan_t p, const void* q, const void* kc, const void* vc, int6
 int moa_append_decode(moa_plan_t p, const void* q, void* kc, void* vc, const void* kn,
                       const void* vn, int64_t pos, void* o, void* ws, size_t ws_bytes,
                       void* stream) {
-  int st = check_decode(p, q, kc, vc, pos, o, ws, ws_bytes, "moa_append_decode");
+  if (p != nullptr && (!kn || !vn))
+    return fail(MOA_EINVAL, "moa_append_decode: k_new and v_new must not be NULL");
+  int st = check_aligned("moa_append_decode", {kn, vn});
   if (st != MOA_OK) return st;
-  if (!kn || !vn) return fail(MOA_EINVAL, "moa_append_decode: k_new and v_new must not be NULL");
+  if ((st = check_decode(p, q, kc, vc, pos, o, ws, ws_bytes, true, "moa_append_decode")) != MOA_OK)
+    return st;
   if (pos >= ((int64_t)1 << 62))
     return fail(MOA_EINVAL, "moa_append_decode: pos out of range");
   hipError_t e =

@@ -172,8 +172,10 @@ size_t moa_decode_workspace_bytes(moa_plan_t plan);
  * the decode partials.  A bounded cache lets a larger batch fit (project
  * page, "Inference speed and memory efficiency"); the same problem with
  * every span equal to N gives the dense cache's figure.  Returns the batch
- * (>= 0) or a negative moa_status (the problem is validated as by
- * moa_plan_create). */
+ * (>= 0, at most INT32_MAX: a plan's batch is int32) or a negative
+ * moa_status (the problem is validated as by moa_plan_create).  Any budget
+ * up to UINT64_MAX is accepted; byte counts that would overflow 64 bits count
+ * as not fitting. */
 int64_t moa_max_batch(const moa_problem* problem, uint64_t budget_bytes);
 
 /* Work-list inspection, for tests.  Prefill items are int32 sextuples

@@ -36,7 +36,10 @@ from .moa_oracle import (  # noqa: F401
     BLOCK,
     span_of,
     spans,
+    ring_pitch,
     ring_offsets,
+    pool_index_k,
+    pool_index_v,
     ring_slot,
     kv_head_of,
     band_mask,

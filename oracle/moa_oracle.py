@@ -61,20 +61,52 @@ def spans(alpha, beta, n):
 # Fixed-size, head-specific KV cache (ring of S_h slots per head)
 # ---------------------------------------------------------------------------
 
-def ring_offsets(span):
+def ring_pitch(s, pitch):
+    """Slots a ring of s slots occupies in the pool when every ring starts on a
+    multiple of `pitch` slots: s rounded up to a multiple of pitch.
+
+    The pages fix only that head h's cache holds S_h slots (project page,
+    "Demo" step 03).  Padding each ring to a whole number of pitch-slot blocks
+    is a layout choice; the slots s .. pitch - 1 past the ring are never
+    attended.  pitch = 1 is the unpadded layout.
+    """
+    s, pitch = int(s), int(pitch)
+    if s < 1 or pitch < 1:
+        raise ValueError("span and pitch must be >= 1")
+    return -(-s // pitch) * pitch
+
+
+def ring_offsets(span, pitch=1):
     """Start of each head's ring inside one sequence's cache block.
 
     Project page, "Demo" step 03 and "Inference speed and memory efficiency":
-    deployment keeps a fixed-size KV cache per head, so head h owns exactly
-    S_h slots.  Heads are laid end to end: offset[h] is the exclusive prefix
-    sum of the spans and a sequence's block holds sum(S) slots.
+    deployment keeps a fixed-size KV cache per head, so head h owns S_h slots.
+    Heads are laid end to end, each ring taking ring_pitch(S_h, pitch) slots:
+    offset[h] is the exclusive prefix sum of those sizes and a sequence's block
+    holds their sum.  With pitch = 1 that is the prefix sum of the spans.
     """
     offset = []
     total = 0
     for s in span:
         offset.append(total)
-        total += int(s)
+        total += ring_pitch(s, pitch)
     return np.array(offset, dtype=np.int64), total
+
+
+def pool_index_k(ring_start, slot, d, head_dim):
+    """Element index of K (slot, d) of a ring that starts at pool slot
+    ring_start: slots are rows of head_dim elements (slot-major)."""
+    return (int(ring_start) + int(slot)) * int(head_dim) + int(d)
+
+
+def pool_index_v(ring_start, slot, d, head_dim, block=32):
+    """Element index of V (slot, d) of a ring that starts at pool slot
+    ring_start: the ring is cut into blocks of `block` consecutive slots, and
+    each block is stored dimension-major ([head_dim][block]), so the slots of
+    one dimension within a block are adjacent.  A layout choice, like the
+    pitch: the pages only fix the ring's size."""
+    slot, d, hd, blk = int(slot), int(d), int(head_dim), int(block)
+    return int(ring_start) * hd + (slot // blk) * blk * hd + d * blk + slot % blk
 
 
 def ring_slot(p, s):

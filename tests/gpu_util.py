@@ -5,6 +5,8 @@ import sys
 import numpy as np
 import torch
 
+import oracle
+
 
 def log(msg):
     """Name the case before each GPU step, so a failing run says which it was."""
@@ -17,22 +19,37 @@ def f64(t):
     return t.detach().to("cpu", torch.float64).numpy()
 
 
-def ring_pitch(s):
-    """Slots a ring of span s occupies in the pool (include/moa.h: multiple of 32)."""
-    return (int(s) + 31) // 32 * 32
+class Layout:
+    """Spans and ring locations of a problem, from the oracle alone (never from a plan).
+
+    seq_spans [B, Hkv]: oracle.spans at each sequence's own length; ring_offsets [B, Hkv]:
+    first slot of each ring, the rings of all sequences laid end to end in (b, h) order at
+    a 32-slot pitch (oracle.ring_offsets); spans [Hkv] when every sequence has length n,
+    else None; total_slots: slots of the whole pool.
+    """
+
+    def __init__(self, alpha, beta, batch, head_dim, n, seq_len=None):
+        lens = [int(n)] * batch if seq_len is None else [int(x) for x in seq_len]
+        self.head_dim, self.batch, self.n_kv_heads = int(head_dim), int(batch), len(alpha)
+        self.seq_len = lens
+        self.seq_spans = np.stack([oracle.spans(alpha, beta, nb) for nb in lens])
+        off, self.total_slots = oracle.ring_offsets(self.seq_spans.ravel(), pitch=32)
+        self.ring_offsets = off.reshape(self.seq_spans.shape)
+        self.spans = self.seq_spans[0].copy() if seq_len is None else None
 
 
 def ring_k(pool, plan, b, h):
-    """[S, D] view of K ring (b, h) in the layout include/moa.h documents."""
+    """[S, D] view of K ring (b, h): slot-major rows (oracle.pool_index_k)."""
     s, d = int(plan.seq_spans[b, h]), plan.head_dim
     base = int(plan.ring_offsets[b, h]) * d
     return pool[base:base + s * d].view(s, d)
 
 
 def ring_v(pool, plan, b, h):
-    """[S, D] copy of V ring (b, h): stored in 32-slot blocks, each [D][32]."""
+    """[S, D] copy of V ring (b, h): stored in 32-slot blocks, each [D][32]
+    (oracle.pool_index_v; tests/test_host.py pins this view to it)."""
     s, d = int(plan.seq_spans[b, h]), plan.head_dim
-    r = ring_pitch(s)
+    r = oracle.ring_pitch(s, 32)
     base = int(plan.ring_offsets[b, h]) * d
     blocks = pool[base:base + r * d].view(r // 32, d, 32)     # [block][dim][slot]
     return blocks.permute(0, 2, 1).reshape(r, d)[:s]

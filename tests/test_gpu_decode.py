@@ -14,7 +14,7 @@ from threadpoolctl import threadpool_limits
 
 import oracle
 import workloads
-from gpu_util import f64, log, max_err, ring_k, ring_positions, ring_v
+from gpu_util import Layout, f64, log, max_err, ring_k, ring_positions, ring_v
 
 pytestmark = pytest.mark.gpu
 
@@ -27,21 +27,22 @@ def _prompt_and_steps(bsz, hq, hkv, n, d, t_steps, seed):
     return kp, vp, qs, ks, vs
 
 
-def _check_rings(plan, kc, vc, kp, vp, ks, vs, n, t_done):
-    """Every slot of every ring holds the bits of the position it should."""
+def _check_rings(lay, kc, vc, kp, vp, ks, vs, n, t_done):
+    """Every slot of every ring holds the bits of the position it should (spans and ring
+    locations from the oracle's layout)."""
     p_last = n - 1 + t_done
     kc_h, vc_h = kc.cpu(), vc.cpu()
-    for b in range(plan.batch):
-        for h in range(plan.n_kv_heads):
-            s = int(plan.spans[h])
+    for b in range(lay.batch):
+        for h in range(lay.n_kv_heads):
+            s = int(lay.spans[h])
             hist_k = torch.cat([kp[b, h], ks[:t_done, b, h]]) if t_done else kp[b, h]
             hist_v = torch.cat([vp[b, h], vs[:t_done, b, h]]) if t_done else vp[b, h]
             pos = np.arange(n + t_done)
             exp_k, held = oracle.ring_expected(hist_k.view(torch.int16).numpy(), pos, s, p_last)
             exp_v, _ = oracle.ring_expected(hist_v.view(torch.int16).numpy(), pos, s, p_last)
             assert (held == ring_positions(s, p_last)).all()
-            assert np.array_equal(ring_k(kc_h, plan, b, h).view(torch.int16).numpy(), exp_k), (b, h)
-            assert np.array_equal(ring_v(vc_h, plan, b, h).contiguous().view(torch.int16).numpy(),
+            assert np.array_equal(ring_k(kc_h, lay, b, h).view(torch.int16).numpy(), exp_k), (b, h)
+            assert np.array_equal(ring_v(vc_h, lay, b, h).contiguous().view(torch.int16).numpy(),
                                   exp_v), (b, h)
 
 
@@ -64,12 +65,13 @@ def test_handoff_append_decode(moa, case):
     bsz, hq, hkv, d, n, alpha, beta, t_steps = CASES[case]
     log(f"decode case {case}: B{bsz} Hq{hq} Hkv{hkv} D{d} N{n} T{t_steps}")
     plan = moa.Plan(bsz, hq, hkv, d, n, alpha, beta)
+    lay = Layout(alpha, beta, bsz, d, n)
     kp, vp, qs, ks, vs = _prompt_and_steps(bsz, hq, hkv, n, d, t_steps, 5000 + 10 * case)
     kc, vc = plan.new_cache()
     ws = plan.new_workspace()
     plan.kv_append(kc, vc, kp.cuda(), vp.cuda(), 0)
     torch.cuda.synchronize()
-    _check_rings(plan, kc, vc, kp, vp, ks, vs, n, 0)
+    _check_rings(lay, kc, vc, kp, vp, ks, vs, n, 0)
     outs = []
     for t in range(t_steps):
         plan.kv_append(kc, vc, ks[t].unsqueeze(2).cuda(), vs[t].unsqueeze(2).cuda(), n + t)
@@ -77,12 +79,12 @@ def test_handoff_append_decode(moa, case):
         plan.decode(qs[t].cuda(), kc, vc, n + t, o, ws)
         outs.append(o)
     torch.cuda.synchronize()
-    _check_rings(plan, kc, vc, kp, vp, ks, vs, n, t_steps)
+    _check_rings(lay, kc, vc, kp, vp, ks, vs, n, t_steps)
     want = oracle.decode(f64(qs), [f64(kp[:, h]) for h in range(hkv)],
-                         [f64(vp[:, h]) for h in range(hkv)], f64(ks), f64(vs), plan.spans, n)
+                         [f64(vp[:, h]) for h in range(hkv)], f64(ks), f64(vs), lay.spans, n)
     got = np.stack([f64(o) for o in outs])
     err = max_err(got, want)
-    log(f"case {case} spans {list(plan.spans)} max abs err {err:.3e}")
+    log(f"case {case} spans {list(lay.spans)} max abs err {err:.3e}")
     assert np.isfinite(got).all()
     assert err <= TOL
 
@@ -154,6 +156,8 @@ def test_decode_full_size_every_head(moa, name):
     w = GQA_3072 if name == "gqa_chunk3072" else workloads.WORKLOADS[name]
     alpha, beta = workloads.rules("c4_decode" if name == "gqa_chunk3072" else name)
     plan = moa.Plan(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, alpha, beta)
+    lay = Layout(alpha, beta, w.batch, w.head_dim, w.n_prompt)
+    assert plan.cache_elems == lay.total_slots * w.head_dim
     log(f"{name}: decode chunk {plan.decode_chunk} slots, {len(plan.decode_chunks())} chunks")
     if name == "gqa_chunk3072":
         assert plan.decode_chunk == 3072
@@ -185,12 +189,12 @@ def test_decode_full_size_every_head(moa, name):
     def check(pair):
         """Worst error of one (b, h) over the steps, and the step it occurs at."""
         b, h = pair
-        s = int(plan.spans[h])
+        s = int(lay.spans[h])
         order = np.argsort(ring_positions(s, n - 1))   # the prompt tail, by position
         hist_k = np.empty((s + t_steps, w.head_dim))
         hist_v = np.empty((s + t_steps, w.head_dim))
-        hist_k[:s] = f64(ring_k(kc_h, plan, b, h))[order]
-        hist_v[:s] = f64(ring_v(vc_h, plan, b, h))[order]
+        hist_k[:s] = f64(ring_k(kc_h, lay, b, h))[order]
+        hist_v[:s] = f64(ring_v(vc_h, lay, b, h))[order]
         res = (0.0, -1)
         for t in range(t_steps):
             hist_k[s + t], hist_v[s + t] = ks64[t, b, h], vs64[t, b, h]

@@ -31,7 +31,8 @@ def test_dense_prefill_is_causal_attention(moa, d):
                                          v.double().repeat_interleave(g, dim=1),
                                          is_causal=True).numpy()
     assert max_err(f64(o), ref) <= 2e-2
-    assert max_err(f64(o), oracle.prefill(f64(q), f64(k), f64(v), plan.spans)) <= 2e-2
+    want = oracle.prefill(f64(q), f64(k), f64(v), oracle.spans([n] * hkv, [0.0] * hkv, n))
+    assert max_err(f64(o), want) <= 2e-2
 
 
 def test_dense_decode_matches_oracle(moa):
@@ -51,5 +52,6 @@ def test_dense_decode_matches_oracle(moa):
         outs.append(o)
     torch.cuda.synchronize()
     want = oracle.decode(f64(qs), [f64(kp[:, h]) for h in range(hkv)],
-                         [f64(vp[:, h]) for h in range(hkv)], f64(ks), f64(vs), plan.spans, n)
+                         [f64(vp[:, h]) for h in range(hkv)], f64(ks), f64(vs),
+                         oracle.spans([n] * hkv, [0.0] * hkv, n), n)
     assert max_err(np.stack([f64(o) for o in outs]), want) <= 2e-2

@@ -35,12 +35,13 @@ PREFILL_CASES = [
 def test_prefill_large_scores(moa, case):
     bsz, hq, hkv, d, n, alpha, beta, dt, scale, handoff = PREFILL_CASES[case]
     plan = moa.Plan(bsz, hq, hkv, d, n, alpha, beta, dtype=dt)
+    spans = oracle.spans(alpha, beta, n)
     q, k, v = workloads.prefill_inputs(bsz, hq, hkv, n, d, dt, 9100 + case)
     # scores grow along the keys, so later tiles keep raising the row max
     ramp = torch.linspace(0.2, 1.0, n).view(1, 1, n, 1)
     q, k = _scaled(q, scale), _scaled((k.float() * ramp).to(k.dtype), scale)
     log(f"prefill large scores case {case}: B{bsz} Hq{hq} Hkv{hkv} D{d} N{n} {dt} x{scale} "
-        f"handoff={handoff} spans {[int(x) for x in plan.spans]}")
+        f"handoff={handoff} spans {[int(x) for x in spans]}")
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     o = torch.empty_like(qd)
     plan.prefill(qd, kd, vd, o)
@@ -51,7 +52,7 @@ def test_prefill_large_scores(moa, case):
     torch.cuda.synchronize()
     got = f64(o)
     assert np.isfinite(got).all()
-    want = oracle.prefill(f64(q), f64(k), f64(v), plan.spans)
+    want = oracle.prefill(f64(q), f64(k), f64(v), spans)
     err = max_err(got, want)
     log(f"case {case}: max abs err {err:.3e}")
     assert err <= TOL[dt]
@@ -74,11 +75,12 @@ DECODE_CASES = [
 def test_decode_large_scores(moa, case, fused):
     bsz, hq, hkv, d, n, alpha, beta, t_steps, scale = DECODE_CASES[case]
     plan = moa.Plan(bsz, hq, hkv, d, n, alpha, beta)
+    spans = oracle.spans(alpha, beta, n)
     _, kp, vp = workloads.prefill_inputs(bsz, hq, hkv, n, d, "bf16", 9200 + case)
     qs, ks, vs = workloads.decode_step_inputs(bsz, hq, hkv, t_steps, d, "bf16", 9300 + case)
     kp, ks, qs = _scaled(kp, scale), _scaled(ks, scale), _scaled(qs, scale)
     log(f"decode large scores case {case} fused={fused}: B{bsz} Hq{hq} Hkv{hkv} D{d} N{n} "
-        f"x{scale} spans {[int(x) for x in plan.spans]} chunk {plan.decode_chunk}")
+        f"x{scale} spans {[int(x) for x in spans]} chunk {plan.decode_chunk}")
     kc, vc = plan.new_cache()
     ws = plan.new_workspace()
     plan.kv_append(kc, vc, kp.cuda(), vp.cuda(), 0)
@@ -95,7 +97,7 @@ def test_decode_large_scores(moa, case, fused):
     got = np.stack([f64(o) for o in outs])
     assert np.isfinite(got).all()
     want = oracle.decode(f64(qs), [f64(kp[:, h]) for h in range(hkv)],
-                         [f64(vp[:, h]) for h in range(hkv)], f64(ks), f64(vs), plan.spans, n)
+                         [f64(vp[:, h]) for h in range(hkv)], f64(ks), f64(vs), spans, n)
     err = max_err(got, want)
     log(f"case {case} fused={fused}: max abs err {err:.3e}")
     assert err <= TOL["bf16"]

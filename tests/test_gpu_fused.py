@@ -18,7 +18,7 @@ from threadpoolctl import threadpool_limits
 
 import oracle
 import workloads
-from gpu_util import f64, log, max_err, ring_k, ring_positions, ring_v
+from gpu_util import Layout, f64, log, max_err, ring_k, ring_positions, ring_v
 
 pytestmark = pytest.mark.gpu
 
@@ -30,21 +30,22 @@ def _bits(t):
     return t.contiguous().view(_BITS[t.dtype]).numpy()
 
 
-def _check_rings(plan, kc, vc, kp, vp, ks, vs, n, t_done):
-    """Every slot holds the bits the oracle says it must after position n - 1 + t_done."""
+def _check_rings(lay, kc, vc, kp, vp, ks, vs, n, t_done):
+    """Every slot holds the bits the oracle says it must after position n - 1 + t_done
+    (spans and ring locations from the oracle's layout)."""
     p_last = n - 1 + t_done
     kc_h, vc_h = kc.cpu(), vc.cpu()
-    for b in range(plan.batch):
-        for h in range(plan.n_kv_heads):
-            s = int(plan.spans[h])
+    for b in range(lay.batch):
+        for h in range(lay.n_kv_heads):
+            s = int(lay.spans[h])
             hist_k = torch.cat([kp[b, h], ks[:t_done, b, h]]) if t_done else kp[b, h]
             hist_v = torch.cat([vp[b, h], vs[:t_done, b, h]]) if t_done else vp[b, h]
             pos = np.arange(n + t_done)
             exp_k, held = oracle.ring_expected(_bits(hist_k), pos, s, p_last)
             exp_v, _ = oracle.ring_expected(_bits(hist_v), pos, s, p_last)
             assert (held == ring_positions(s, p_last)).all()
-            assert np.array_equal(_bits(ring_k(kc_h, plan, b, h)), exp_k), (b, h)
-            assert np.array_equal(_bits(ring_v(vc_h, plan, b, h)), exp_v), (b, h)
+            assert np.array_equal(_bits(ring_k(kc_h, lay, b, h)), exp_k), (b, h)
+            assert np.array_equal(_bits(ring_v(vc_h, lay, b, h)), exp_v), (b, h)
 
 
 HANDOFF_CASES = [
@@ -65,6 +66,7 @@ def test_prefill_handoff_small(moa, case):
     bsz, hq, hkv, d, n, alpha, beta, dt = HANDOFF_CASES[case]
     log(f"prefill_handoff case {case}: B{bsz} Hq{hq} Hkv{hkv} D{d} N{n} {dt}")
     plan = moa.Plan(bsz, hq, hkv, d, n, alpha, beta, dtype=dt)
+    lay = Layout(alpha, beta, bsz, d, n)
     q, k, v = workloads.prefill_inputs(bsz, hq, hkv, n, d, dt, 7000 + case)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     o_plain = torch.empty_like(qd)
@@ -73,12 +75,12 @@ def test_prefill_handoff_small(moa, case):
     kc, vc = plan.new_cache()
     plan.prefill_handoff(qd, kd, vd, o, kc, vc)
     torch.cuda.synchronize()
-    want = oracle.prefill(f64(q), f64(k), f64(v), plan.spans)
+    want = oracle.prefill(f64(q), f64(k), f64(v), lay.spans)
     err = max_err(f64(o), want)
-    log(f"case {case} spans {list(plan.spans)} max abs err {err:.3e}")
+    log(f"case {case} spans {list(lay.spans)} max abs err {err:.3e}")
     assert err <= TOL[dt]
     assert torch.equal(o, o_plain)
-    _check_rings(plan, kc, vc, k, v, None, None, n, 0)
+    _check_rings(lay, kc, vc, k, v, None, None, n, 0)
 
 
 APPEND_CASES = [
@@ -102,6 +104,7 @@ def test_append_decode_small(moa, case):
     bsz, hq, hkv, d, n, alpha, beta, t_steps = APPEND_CASES[case]
     log(f"append_decode case {case}: B{bsz} Hq{hq} Hkv{hkv} D{d} N{n} T{t_steps}")
     plan = moa.Plan(bsz, hq, hkv, d, n, alpha, beta)
+    lay = Layout(alpha, beta, bsz, d, n)
     _, kp, vp = workloads.prefill_inputs(bsz, hq, hkv, n, d, "bf16", 8000 + 10 * case)
     qs, ks, vs = workloads.decode_step_inputs(bsz, hq, hkv, t_steps, d, "bf16", 8001 + 10 * case)
     kc, vc = plan.new_cache()
@@ -119,13 +122,13 @@ def test_append_decode_small(moa, case):
         plan.decode(q, kc2, vc2, n + t, o2, ws2)
         torch.cuda.synchronize()
         assert max_err(f64(o), f64(o2)) <= TOL["bf16"], t
-        _check_rings(plan, kc, vc, kp, vp, ks, vs, n, t + 1)
+        _check_rings(lay, kc, vc, kp, vp, ks, vs, n, t + 1)
         outs.append(o)
     want = oracle.decode(f64(qs), [f64(kp[:, h]) for h in range(hkv)],
-                         [f64(vp[:, h]) for h in range(hkv)], f64(ks), f64(vs), plan.spans, n)
+                         [f64(vp[:, h]) for h in range(hkv)], f64(ks), f64(vs), lay.spans, n)
     got = np.stack([f64(o) for o in outs])
     err = max_err(got, want)
-    log(f"case {case} spans {list(plan.spans)} max abs err {err:.3e}")
+    log(f"case {case} spans {list(lay.spans)} max abs err {err:.3e}")
     assert err <= TOL["bf16"]
 
 
@@ -175,6 +178,8 @@ def test_prefill_handoff_full_size(moa, name):
     w = workloads.WORKLOADS[name]
     alpha, beta = workloads.rules(name)
     plan = moa.Plan(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, alpha, beta)
+    lay = Layout(alpha, beta, w.batch, w.head_dim, w.n_prompt)
+    assert plan.cache_elems == lay.total_slots * w.head_dim
     n, d = w.n_prompt, w.head_dim
     log(f"{name}: prefill_handoff at full size")
     shape_q = (w.batch, w.n_q_heads, n, d)
@@ -192,23 +197,25 @@ def test_prefill_handoff_full_size(moa, name):
     kc_h, vc_h, k_h, v_h = kc.cpu(), vc.cpu(), k.cpu(), v.cpu()
     for b in range(w.batch):
         for h in range(w.n_kv_heads):
-            s = int(plan.spans[h])
+            s = int(lay.spans[h])
             pos = [oracle.ring_slot(p, s) for p in range(n - s, n)]
             want_slot_of = np.array(pos)
             held = np.empty(s, dtype=np.int64)
             held[want_slot_of] = np.arange(n - s, n)
-            assert np.array_equal(_bits(ring_k(kc_h, plan, b, h)), _bits(k_h[b, h][held])), (b, h)
-            assert np.array_equal(_bits(ring_v(vc_h, plan, b, h)), _bits(v_h[b, h][held])), (b, h)
+            assert np.array_equal(_bits(ring_k(kc_h, lay, b, h)), _bits(k_h[b, h][held])), (b, h)
+            assert np.array_equal(_bits(ring_v(vc_h, lay, b, h)), _bits(v_h[b, h][held])), (b, h)
     log(f"{name}: o identical, {w.batch * w.n_kv_heads} rings exact")
 
 
-@pytest.mark.parametrize("name", ["c2_decode", "c4_decode"])
+@pytest.mark.parametrize("name", ["c2_decode", "c3_decode", "c4_decode"])
 def test_append_decode_full_size_every_head(moa, name):
     """Full-size rings, three fused steps, every (b, h) of every step against the oracle; the
     new positions' slots of every ring hold the new bits."""
     w = workloads.WORKLOADS[name]
     alpha, beta = workloads.rules(name)
     plan = moa.Plan(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, alpha, beta)
+    lay = Layout(alpha, beta, w.batch, w.head_dim, w.n_prompt)
+    assert plan.cache_elems == lay.total_slots * w.head_dim
     log(f"{name}: filling {2 * plan.cache_elems * 2 / 1e9:.2f} GB of rings")
     kc = workloads.device_normal_(torch.empty(plan.cache_elems, dtype=torch.bfloat16,
                                               device="cuda"), 83)
@@ -236,12 +243,12 @@ def test_append_decode_full_size_every_head(moa, name):
     def check(pair):
         """Worst error of one (b, h) over the steps and the step it occurs at; ring bits."""
         b, h = pair
-        s = int(plan.spans[h])
+        s = int(lay.spans[h])
         order = np.argsort(ring_positions(s, n - 1))
         hist_k = np.empty((s + t_steps, w.head_dim))
         hist_v = np.empty((s + t_steps, w.head_dim))
-        hist_k[:s] = f64(ring_k(kc0, plan, b, h))[order]
-        hist_v[:s] = f64(ring_v(vc0, plan, b, h))[order]
+        hist_k[:s] = f64(ring_k(kc0, lay, b, h))[order]
+        hist_v[:s] = f64(ring_v(vc0, lay, b, h))[order]
         res = (0.0, -1)
         for t in range(t_steps):
             hist_k[s + t], hist_v[s + t] = ks64[t, b, h], vs64[t, b, h]
@@ -250,8 +257,8 @@ def test_append_decode_full_size_every_head(moa, name):
             res = max(res, (max_err(outs64[t][b, h * g:(h + 1) * g], want), t))
         # the last min(s, T) new positions sit in their slots
         slots_ok = all(
-            torch.equal(ring_k(kc_h, plan, b, h)[oracle.ring_slot(n + t, s)], ks[t, b, h]) and
-            torch.equal(ring_v(vc_h, plan, b, h)[oracle.ring_slot(n + t, s)], vs[t, b, h])
+            torch.equal(ring_k(kc_h, lay, b, h)[oracle.ring_slot(n + t, s)], ks[t, b, h]) and
+            torch.equal(ring_v(vc_h, lay, b, h)[oracle.ring_slot(n + t, s)], vs[t, b, h])
             for t in range(max(0, t_steps - s), t_steps))
         return res, slots_ok
 

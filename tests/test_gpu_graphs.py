@@ -21,7 +21,7 @@ def test_prefill_handoff_and_append_decode_in_graphs(moa, hq, hkv, d):
     bsz, n = 2, 1500
     alpha, beta = [0, 300, 64, 0][:hkv], [0.5, 0.0, 0.0, 1.0][:hkv]
     plan = moa.Plan(bsz, hq, hkv, d, n, alpha, beta)
-    log(f"graphs: B{bsz} Hq{hq} Hkv{hkv} D{d} N{n} spans {[int(x) for x in plan.spans]}")
+    log(f"graphs: B{bsz} Hq{hq} Hkv{hkv} D{d} N{n} decode chunk {plan.decode_chunk}")
     q, k, v = (x.cuda() for x in workloads.prefill_inputs(bsz, hq, hkv, n, d, "bf16", 7300))
     qs, ks, vs = (x.cuda() for x in workloads.decode_step_inputs(bsz, hq, hkv, 1, d, "bf16", 7301))
 

@@ -28,11 +28,12 @@ def test_layers_from_rules_file(moa):
     lens = [1200, 700]
     bsz, hq, hkv, d, n, t_steps = 2, 16, 8, 64, max(lens), 2
     plans = rs.plans(bsz, hq, d, n, seq_len=lens)
-    assert len({tuple(p.seq_spans[0]) for p in plans}) == 3   # the layers' spans differ
+    # the layers' spans differ
+    assert len({tuple(oracle.spans(a, b, lens[0])) for a, b in rs.layers}) == 3
     worst = 0.0
     try:
         for layer, plan in enumerate(plans):
-            log(f"layer {layer}: spans {list(plan.seq_spans[0])} / {list(plan.seq_spans[1])}")
+            log(f"layer {layer}: lens {lens}, decode chunk {plan.decode_chunk}")
             q, k, v = workloads.prefill_inputs(bsz, hq, hkv, n, d, "bf16", 9500 + layer)
             qs, ks, vs = workloads.decode_step_inputs(bsz, hq, hkv, t_steps, d, "bf16",
                                                       9600 + layer)
@@ -50,8 +51,8 @@ def test_layers_from_rules_file(moa):
             got_d = np.stack([f64(x) for x in outs])
             for b, nb in enumerate(lens):
                 pad = n - nb
-                spans = rs.spans(nb)[layer]
-                assert list(plan.seq_spans[b]) == list(spans)
+                # the oracle's own spans for this layer's rules at the sequence's length
+                spans = oracle.spans(*rs.layers[layer], nb)
                 want = oracle.prefill(f64(q[b:b + 1, :, pad:]), f64(k[b:b + 1, :, pad:]),
                                       f64(v[b:b + 1, :, pad:]), spans)
                 err_p = max_err(f64(o[b:b + 1, :, pad:]), want)

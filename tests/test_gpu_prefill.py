@@ -31,11 +31,12 @@ def test_c0_tiny_prefill_fp32(moa):
     log("prefill c0 fp32 B1 H4 D64 N512")
     plan = moa.Plan(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, alpha, beta,
                     dtype="f32")
-    assert list(plan.spans) == [64, 128, 256, 512]
+    spans = oracle.spans(alpha, beta, w.n_prompt)
+    assert list(spans) == [64, 128, 256, 512]
     q, k, v = workloads.prefill_inputs(w.batch, w.n_q_heads, w.n_kv_heads, w.n_prompt,
                                        w.head_dim, "f32", w.data_seed)
     o = _run_prefill(moa, plan, q, k, v)
-    want = oracle.prefill(f64(q), f64(k), f64(v), plan.spans)
+    want = oracle.prefill(f64(q), f64(k), f64(v), spans)
     err = max_err(f64(o), want)
     log(f"c0 max abs err {err:.3e}")
     assert err <= TOL["f32"]
@@ -67,9 +68,10 @@ def test_prefill_small(moa, case):
     plan = moa.Plan(bsz, hq, hkv, d, n, alpha, beta, dtype=dt)
     q, k, v = workloads.prefill_inputs(bsz, hq, hkv, n, d, dt, 3000 + case)
     o = _run_prefill(moa, plan, q, k, v)
-    want = oracle.prefill(f64(q), f64(k), f64(v), plan.spans)
+    spans = oracle.spans(alpha, beta, n)
+    want = oracle.prefill(f64(q), f64(k), f64(v), spans)
     err = max_err(f64(o), want)
-    log(f"case {case} spans {list(plan.spans)} max abs err {err:.3e}")
+    log(f"case {case} spans {list(spans)} max abs err {err:.3e}")
     assert np.isfinite(f64(o)).all()
     assert err <= TOL[dt]
 
@@ -78,7 +80,7 @@ def test_prefill_small(moa, case):
 def test_prefill_span_one_returns_v_exactly(moa, dt):
     log(f"prefill span-1 {dt}")
     plan = moa.Plan(2, 4, 2, 128, 200, [0, 0], [0.0, 0.0], dtype=dt)
-    assert list(plan.spans) == [1, 1]
+    assert list(oracle.spans([0, 0], [0.0, 0.0], 200)) == [1, 1]
     q, k, v = workloads.prefill_inputs(2, 4, 2, 200, 128, dt, 41)
     o = _run_prefill(moa, plan, q, k, v).cpu()
     vrep = v.repeat_interleave(2, dim=1)
@@ -103,9 +105,10 @@ def test_c1_prefill_full_size_sampled_rows(moa):
                                        w.head_dim, "bf16", w.data_seed)
     log("prefill c1 full size")
     o = _run_prefill(moa, plan, q, k, v).cpu()
+    spans = oracle.spans(alpha, beta, w.n_prompt)
     worst = 0.0
     for h in range(w.n_q_heads):
-        s = int(plan.spans[h])
+        s = int(spans[h])
         rows = sample_rows(w.n_prompt, s, 24, 100 + h)
         want = oracle.prefill_rows(f64(q[0, h, rows]), f64(k[0, h]), f64(v[0, h]), s, rows)
         err = max_err(f64(o[0, h, rows]), want)
@@ -125,9 +128,10 @@ def test_c1_prefill_full_size_every_row(moa):
                                        w.head_dim, "bf16", w.data_seed)
     log("prefill c1 full size, every row")
     o = _run_prefill(moa, plan, q, k, v).cpu()
+    spans = oracle.spans(alpha, beta, w.n_prompt)
     worst = 0.0
     for h in range(w.n_q_heads):
-        s = int(plan.spans[h])
+        s = int(spans[h])
         want = oracle.prefill(f64(q[:, h:h + 1]), f64(k[:, h:h + 1]), f64(v[:, h:h + 1]), [s])
         err = max_err(f64(o[:, h:h + 1]), want)
         worst = max(worst, err)
@@ -154,9 +158,10 @@ def test_c4_prefill_full_size_row_blocks(moa):
     torch.cuda.synchronize()
     n, g, blk = w.n_prompt, w.n_q_heads // w.n_kv_heads, 128
     rng = np.random.Generator(np.random.PCG64(204))
+    spans = oracle.spans(alpha, beta, n)
     worst = 0.0
     for hk in range(w.n_kv_heads):
-        s = int(plan.spans[hk])
+        s = int(spans[hk])
         kh, vh = f64(k[0, hk]), f64(v[0, hk])
         for hq in range(hk * g, hk * g + g):
             starts = [0, min(max(0, s - blk // 2), n - blk), int(rng.integers(0, n - blk)), n - blk]

@@ -17,7 +17,7 @@ def test_plan_shared_by_two_streams(moa):
     bsz, hq, hkv, d, n, steps = 3, 8, 4, 128, 1500, 4
     alpha, beta = [0, 64, 512, 0], [0.25, 0.0, 0.0, 1.0]
     plan = moa.Plan(bsz, hq, hkv, d, n, alpha, beta)
-    log(f"two streams: spans {[int(x) for x in plan.spans]}, decode chunk {plan.decode_chunk}")
+    log(f"two streams: decode chunk {plan.decode_chunk}")
     inputs = [workloads.prefill_inputs(bsz, hq, hkv, n, d, "bf16", 7100 + i) for i in range(2)]
     steps_in = [workloads.decode_step_inputs(bsz, hq, hkv, steps, d, "bf16", 7200 + i)
                 for i in range(2)]

@@ -77,17 +77,36 @@ def test_spans_random_doubles(moa):
         assert list(moa.spans(alpha, beta, n)) == list(oracle.spans(alpha, beta, n))
 
 
-def _pitch(s):
-    """Ring pitch of the pool layout (include/moa.h): span rounded up to 32 slots."""
-    return [(int(x) + 31) // 32 * 32 for x in s]
-
-
 def test_ring_offsets_bit_exact(moa):
     span = np.array([1, 64, 7, 8192, 3, 65536, 33], dtype=np.int32)
     off, tot = moa.ring_offsets(span)
-    o_off, o_tot = oracle.ring_offsets(_pitch(span))
+    o_off, o_tot = oracle.ring_offsets(span, pitch=32)
     assert list(off) == list(o_off) and tot == o_tot
-    assert all(p >= s and p - s < 32 for p, s in zip(_pitch(span), span))
+
+
+def test_ring_view_helpers_follow_the_oracle_layout():
+    """The GPU tests read rings through gpu_util's tensor views; on a pool whose every element
+    holds its own index, those views give exactly the oracle's K and V element indices."""
+    import torch
+
+    from gpu_util import ring_k, ring_v
+
+    class _Plan:
+        head_dim = 64
+        seq_spans = np.array([[1, 33], [100, 64]])
+        ring_offsets = np.zeros((2, 2), dtype=np.int64)
+
+    spans = _Plan.seq_spans.ravel()
+    off, total = oracle.ring_offsets(spans, pitch=32)
+    _Plan.ring_offsets = off.reshape(2, 2)
+    pool = torch.arange(total * _Plan.head_dim, dtype=torch.int64)
+    for b in range(2):
+        for h in range(2):
+            start, sp = int(_Plan.ring_offsets[b, h]), int(_Plan.seq_spans[b, h])
+            want_k = [[oracle.pool_index_k(start, sl, e, 64) for e in range(64)] for sl in range(sp)]
+            want_v = [[oracle.pool_index_v(start, sl, e, 64) for e in range(64)] for sl in range(sp)]
+            assert ring_k(pool, _Plan, b, h).tolist() == want_k
+            assert ring_v(pool, _Plan, b, h).tolist() == want_v
 
 
 @pytest.mark.parametrize("name", sorted(workloads.WORKLOADS))
@@ -98,7 +117,7 @@ def test_workload_plan_tables(moa, name):
                     dtype=w.dtype, host_only=True)
     s = oracle.spans(alpha, beta, w.n_prompt)
     assert list(plan.spans) == list(s)
-    off, tot = oracle.ring_offsets(_pitch(s))
+    off, tot = oracle.ring_offsets(s, pitch=32)
     assert list(plan.offsets) == list(off) and plan.slots_per_seq == tot
     assert plan.cache_elems == w.batch * tot * w.head_dim
     if name == "c0_prefill":
@@ -291,6 +310,51 @@ def test_max_batch_budget(moa, name):
     assert abs(b_dense / b_moa - density) < 0.02
 
 
+def test_max_batch_huge_budgets(moa):
+    """Budgets near 2^64 return at once, capped at the largest batch a plan accepts (int32);
+    the byte counts never wrap."""
+    import time
+    alpha, beta = workloads.rules("c2_decode")
+    w = workloads.WORKLOADS["c2_decode"]
+    t0 = time.perf_counter()
+    for budget in (2**64 - 1, 2**63, 2**62):
+        b = moa.max_batch(w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, alpha, beta, "bf16",
+                          budget)
+        assert 0 < b <= 2**31 - 1
+    assert moa.max_batch(w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, alpha, beta, "bf16",
+                         2**64 - 1) == 2**31 - 1
+    # a tiny model under a huge budget: the cap, not a wrapped product
+    assert moa.max_batch(1, 1, 64, 1, [0], [0.0], "bf16", 2**64 - 1) == 2**31 - 1
+    # 2^62 bytes / ~136 MB per C2 sequence is about 3.4e10 sequences: capped
+    assert moa.max_batch(w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, alpha, beta, "bf16",
+                         2**62) == 2**31 - 1
+    assert time.perf_counter() - t0 < 5.0
+
+
+def test_misaligned_pointers_are_rejected(moa):
+    """Every compute entry point refuses device pointers that are not 16-byte aligned before any
+    device work (the check precedes the plan's device checks, so a host-only plan shows it)."""
+    plan = moa.Plan(1, 2, 2, 64, 50, [0, 0], [1.0, 1.0], host_only=True)
+    lib = moa._lib
+    ok, bad = ctypes.c_void_p(4096), ctypes.c_void_p(4096 + 8)
+    calls = {
+        "moa_prefill": lambda x: lib.moa_prefill(plan._h, ok, ok, x, ok, None),
+        "moa_prefill_handoff": lambda x: lib.moa_prefill_handoff(plan._h, ok, ok, ok, ok, ok, x,
+                                                                 None),
+        "moa_kv_append": lambda x: lib.moa_kv_append(plan._h, ok, ok, x, ok, 0, 1, None),
+        "moa_decode": lambda x: lib.moa_decode(plan._h, ok, ok, ok, 50, ok, x, 1 << 30, None),
+        "moa_append_decode": lambda x: lib.moa_append_decode(plan._h, ok, ok, ok, x, ok, 50, ok, ok,
+                                                             1 << 30, None),
+    }
+    for name, call in calls.items():
+        assert call(bad) == moa.MOA_EINVAL, name
+        assert "16-byte aligned" in moa.last_error() and name in moa.last_error(), name
+        # aligned pointers get past the check, to the host-only refusal
+        assert call(ok) == moa.MOA_EINVAL, name
+        assert "HOST_ONLY" in moa.last_error(), name
+    plan.close()
+
+
 # ---------------------------------------------------------------------------
 # error paths (checked before any device work, so they run without a GPU)
 # ---------------------------------------------------------------------------
@@ -429,12 +493,13 @@ def test_ragged_plan_tables(moa, case):
     plan = moa.Plan(len(lens), hq, hkv, d, n, alpha, beta, seq_len=lens, host_only=True)
     assert plan.ragged and plan.spans is None
     assert list(plan.seq_len) == lens
-    pitches = []
+    all_spans = []
     for b, nb in enumerate(lens):
-        assert list(plan.seq_spans[b]) == list(oracle.spans(alpha, beta, nb)), b
-        pitches += _pitch(plan.seq_spans[b])
-    # rings of sequence 0, then sequence 1, ...; each head's ring at the prefix sum of pitches
-    off, tot = oracle.ring_offsets(pitches)
+        s = oracle.spans(alpha, beta, nb)
+        assert list(plan.seq_spans[b]) == list(s), b
+        all_spans += list(s)
+    # rings of sequence 0, then sequence 1, ...: one block of 32-slot-pitch rings
+    off, tot = oracle.ring_offsets(all_spans, pitch=32)
     assert list(plan.ring_offsets.reshape(-1)) == list(off)
     assert plan.cache_elems == tot * d
     with pytest.raises(moa.MoaError) as e:

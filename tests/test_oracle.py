@@ -147,6 +147,47 @@ def test_ring_offsets_prefix_sum():
     assert (covered == 1).all()
 
 
+def check_ring_layout():
+    """Ring pitch, offsets and pool indices against values worked by hand from the layout's
+    statement and against the properties the layout must have: rings of whole pitch blocks
+    that tile the sequence's block without overlap, and K/V element maps that are bijections
+    onto the ring's region with the adjacency each layout promises."""
+    # by hand: spans 1, 64, 7, 33 at a 32-slot pitch take 32, 64, 32, 64 slots
+    off, total = oracle.ring_offsets([1, 64, 7, 33], pitch=32)
+    assert list(off) == [0, 32, 96, 128] and total == 192
+    off, total = oracle.ring_offsets([5, 1, 64, 7])      # unpadded: prefix sums of the spans
+    assert list(off) == [0, 5, 6, 70] and total == 77
+    rng = np.random.Generator(np.random.PCG64(17))
+    for pitch in (1, 32, 64):
+        span = [int(x) for x in rng.integers(1, 300, 12)] + [1, pitch, pitch + 1]
+        off, total = oracle.ring_offsets(span, pitch=pitch)
+        covered = np.zeros(total, dtype=int)
+        for h, sp in enumerate(span):
+            r = oracle.ring_pitch(sp, pitch)
+            assert r % pitch == 0 and 0 <= r - sp < pitch
+            assert off[h] % pitch == 0
+            covered[off[h]:off[h] + r] += 1
+        assert (covered == 1).all()
+    # element maps: each ring's slots x dims fill [start*D, (start+R)*D) exactly once
+    for d in (64, 128):
+        for start, sp in ((0, 1), (32, 33), (96, 100), (64, 64)):
+            r = oracle.ring_pitch(sp, 32)
+            for fn in (oracle.pool_index_k, oracle.pool_index_v):
+                idx = sorted(fn(start, sl, e, d) for sl in range(r) for e in range(d))
+                assert idx == list(range(start * d, (start + r) * d)), (fn.__name__, d, sp)
+            for sl in range(r):
+                # K: a slot's dims are one contiguous row
+                assert oracle.pool_index_k(start, sl, d - 1, d) - oracle.pool_index_k(start, sl, 0, d) == d - 1
+                # V: within a 32-slot block, consecutive slots of one dim are adjacent
+                if sl % 32 != 31 and sl + 1 < r:
+                    assert (oracle.pool_index_v(start, sl + 1, 5, d)
+                            == oracle.pool_index_v(start, sl, 5, d) + 1)
+
+
+def test_ring_layout():
+    check_ring_layout()
+
+
 @pytest.mark.parametrize("s", [1, 2, 5, 64, 100])
 def test_ring_holds_last_s_positions(s):
     """After positions 0..p are written in order, the ring holds exactly (p-s, p], each once."""
@@ -338,7 +379,8 @@ def test_decode_equals_prefill_row():
 
 PINS = [check_worked_example, check_spans_bruteforce, check_full_span_is_causal_sdpa,
         check_band_vs_tril_triu_mask, check_span_one_returns_v, check_rows_are_stochastic,
-        check_bruteforce_tiny, check_gqa_equals_repeated_kv, check_decode_equals_prefill_row]
+        check_bruteforce_tiny, check_gqa_equals_repeated_kv, check_decode_equals_prefill_row,
+        check_ring_layout]
 
 
 def _mut_window_wide(s, n):
@@ -406,6 +448,16 @@ def _mut_block_keys_late(q_rows, k, v, s, i0, scale=None):
         out[a] = (e / e.sum()) @ vv
     return out
 
+def _mut_ring_pitch_floor(s, pitch):
+    return max(1, int(s) // int(pitch)) * int(pitch)
+
+
+def _mut_pool_index_v_dim_stride(ring_start, slot, d, head_dim, block=32):
+    """Dimension stride of a whole row instead of one block's width."""
+    return (int(ring_start) * int(head_dim) + (int(slot) // block) * block * int(head_dim)
+            + int(d) * int(head_dim) + int(slot) % block)
+
+
 MUTATIONS = {
     "window_wide": ("band_mask", _mut_window_wide),
     "window_narrow": ("band_mask", _mut_window_narrow),
@@ -417,6 +469,8 @@ MUTATIONS = {
     "no_scale": ("attention_probs", _mut_no_scale),
     "swap_kv": ("prefill", _mut_swap_kv_prefill),
     "block_keys_late": ("prefill_row_block", _mut_block_keys_late),
+    "ring_pitch_floor": ("ring_pitch", _mut_ring_pitch_floor),
+    "pool_v_dim_stride": ("pool_index_v", _mut_pool_index_v_dim_stride),
 }
 
 
