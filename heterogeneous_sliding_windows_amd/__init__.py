@@ -42,7 +42,8 @@ EXPORTS = ("moa_spans", "moa_ring_offsets", "moa_plan_create", "moa_plan_create_
            "moa_decode_workspace_bytes", "moa_max_batch",
            "moa_plan_prefill_items", "moa_plan_decode_chunks", "moa_plan_decode_chunk",
            "moa_prefill", "moa_prefill_handoff", "moa_kv_append", "moa_decode",
-           "moa_append_decode", "moa_last_error", "moa_version")
+           "moa_append_decode", "moa_append_decode_static", "moa_static_workspace_bytes",
+           "moa_last_error", "moa_version")
 
 
 class _Problem(ctypes.Structure):
@@ -78,6 +79,8 @@ _sig = {
     "moa_decode": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int64, _P, _P, ctypes.c_size_t, _P]),
     "moa_append_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int64, _P, _P,
                                          ctypes.c_size_t, _P]),
+    "moa_append_decode_static": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int64, _P, _P]),
+    "moa_static_workspace_bytes": (ctypes.c_size_t, []),
     "moa_last_error": (ctypes.c_char_p, []),
     "moa_version": (ctypes.c_char_p, []),
 }
@@ -145,6 +148,11 @@ def max_batch(n_q_heads, n_kv_heads, head_dim, n_prompt, alpha, beta, dtype, bud
     pr = _Problem(1, int(n_q_heads), int(n_kv_heads), int(head_dim), int(n_prompt), ap, bp,
                   DTYPES[dtype])
     return _check(_lib.moa_max_batch(ctypes.byref(pr), int(budget_bytes)))
+
+
+def static_workspace_bytes():
+    """Size of the fixed scratch behind Plan.append_decode_static."""
+    return int(_lib.moa_static_workspace_bytes())
 
 
 def _stream(stream):
@@ -304,6 +312,17 @@ class Plan:
                 self._t(k_new, (B, Hk, D), "k_new"), self._t(v_new, (B, Hk, D), "v_new"))
         _check(_lib.moa_append_decode(self._h, *args, int(pos), self._t(o, (B, Hq, D), "o"), ws,
                                       ws_bytes, _stream(stream)))
+        return o
+
+    def append_decode_static(self, q, k_cache, v_cache, k_new, v_new, pos, o, stream=None):
+        """append_decode() with the library's fixed decode scratch instead of a workspace
+        (moa_append_decode_static: allocates nothing; calls on one GPU share the scratch)."""
+        B, Hq, Hk, D = self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim
+        args = (self._t(q, (B, Hq, D), "q"), self._t(k_cache, self.cache_shape(), "k_cache"),
+                self._t(v_cache, self.cache_shape(), "v_cache"),
+                self._t(k_new, (B, Hk, D), "k_new"), self._t(v_new, (B, Hk, D), "v_new"))
+        _check(_lib.moa_append_decode_static(self._h, *args, int(pos),
+                                             self._t(o, (B, Hq, D), "o"), _stream(stream)))
         return o
 
     def new_cache(self):

@@ -43,11 +43,44 @@
 // measured several times dearer than the same writes in a phase of their own.
 
 #include <cfloat>
+#include <mutex>
 
 #include "moa_device.h"
 #include "moa_internal.h"
 
 namespace moa {
+
+// Fixed decode scratch for callers that cannot allocate (moa_append_decode_static).
+// Each GPU the library runs on holds its own copy, at its own address, until the
+// process ends.  In host code `scratch` names a host-side stand-in, not device
+// memory: the device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[kStaticWsBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+hipError_t static_workspace(void** out) {
+  *out = nullptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 namespace {
 
 constexpr int kWaves = 4;

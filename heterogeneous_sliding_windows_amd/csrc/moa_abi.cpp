@@ -271,8 +271,9 @@ int check_prefill(moa_plan_t p, const void* q, const void* k, const void* v, con
   return set_device(p);
 }
 
-// Checks shared by moa_decode and moa_append_decode (need_ws = false skips
-// the workspace checks).
+// Checks shared by moa_decode, moa_append_decode and moa_append_decode_static
+// (a null ws with ws_bytes = 0 skips the workspace checks: the static variant
+// brings its own).
 int check_decode(moa_plan_t p, const void* q, const void* kc, const void* vc, int64_t pos,
                  const void* o, const void* ws, size_t ws_bytes, bool need_ws, const char* who) {
   int st = check_plan(p, false);
@@ -626,6 +627,34 @@ int moa_append_decode(moa_plan_t p, const void* q, void* kc, void* vc, const voi
   if (e != hipSuccess) return hip_fail(e, "append_decode launch");
   return MOA_OK;
 }
+
+int moa_append_decode_static(moa_plan_t p, const void* q, void* kc, void* vc, const void* kn,
+                             const void* vn, int64_t pos, void* o, void* stream) {
+  // the size check comes first: it needs no device and names the limit
+  if (p != nullptr && moa::decode_ws_bytes(*p) > moa::kStaticWsBytes)
+    return fail(MOA_EWORKSPACE,
+                "moa_append_decode_static: the plan needs %zu bytes of decode scratch, more than "
+                "the fixed %zu (use moa_append_decode with a workspace)",
+                moa::decode_ws_bytes(*p), moa::kStaticWsBytes);
+  // the other checks are moa_append_decode's; the workspace is the fixed scratch
+  if (p != nullptr && (!kn || !vn))
+    return fail(MOA_EINVAL, "moa_append_decode_static: k_new and v_new must not be NULL");
+  int st = check_aligned("moa_append_decode_static", {kn, vn});
+  if (st != MOA_OK) return st;
+  if ((st = check_decode(p, q, kc, vc, pos, o, nullptr, 0, false, "moa_append_decode_static")) !=
+      MOA_OK)
+    return st;
+  if (pos >= ((int64_t)1 << 62))
+    return fail(MOA_EINVAL, "moa_append_decode_static: pos out of range");
+  void* ws = nullptr;
+  hipError_t e = moa::static_workspace(&ws);
+  if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress (decode scratch)");
+  e = moa::launch_append_decode_bf16(*p, q, kc, vc, kn, vn, pos, o, ws, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "append_decode_static launch");
+  return MOA_OK;
+}
+
+size_t moa_static_workspace_bytes(void) { return moa::kStaticWsBytes; }
 
 const char* moa_last_error(void) { return g_last_error.c_str(); }
 

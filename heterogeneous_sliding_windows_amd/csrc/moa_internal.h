@@ -101,6 +101,12 @@ hipError_t launch_append_decode_bf16(const moa_plan& p, const void* q, void* kc,
                                      const void* kn, const void* vn, int64_t pos, void* o,
                                      void* ws, hipStream_t s);
 
+// Size of the fixed device scratch behind moa_append_decode_static (one copy
+// per GPU, held until the process ends), and its address on the current
+// device (looked up once per device).
+constexpr size_t kStaticWsBytes = (size_t)16 << 20;
+hipError_t static_workspace(void** ptr);
+
 // Workspace layout of the split-K decode: float o[n_chunks][G][D], then
 // float2 ml[n_chunks][G] (running max, sum), chunks of all sequences.
 struct DecodeWs {

@@ -284,6 +284,28 @@ int moa_append_decode(moa_plan_t plan, const void* q, void* k_cache, void* v_cac
                       const void* k_new, const void* v_new, int64_t pos, void* o,
                       void* workspace, size_t ws_bytes, void* stream);
 
+/* moa_append_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels, with the split-K partials kept in a fixed
+ * scratch array inside the library instead of a caller workspace.  The caller
+ * still passes inputs, caches and o.  The call allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine); its first call on a device looks up
+ * that device's copy of the scratch once.
+ *  - Limit: plans whose moa_decode_workspace_bytes exceeds
+ *    moa_static_workspace_bytes() (16 MiB) are rejected with MOA_EWORKSPACE
+ *    before anything is enqueued.
+ *  - Each GPU holds one scratch array until the process ends, shared by every
+ *    call on that GPU, whatever the plan or stream: calls that overlap on one
+ *    GPU race (order them on one stream or synchronise).  The scratch needs no
+ *    initial contents; each call writes every partial it reads.
+ * Other arguments and errors: those of moa_append_decode. */
+int moa_append_decode_static(moa_plan_t plan, const void* q, void* k_cache, void* v_cache,
+                             const void* k_new, const void* v_new, int64_t pos, void* o,
+                             void* stream);
+
+/* Bytes of the fixed scratch behind moa_append_decode_static (16 MiB). */
+size_t moa_static_workspace_bytes(void);
+
 /* Message of the last failing call on this thread ("" if none). */
 const char* moa_last_error(void);
 

@@ -345,6 +345,8 @@ def test_misaligned_pointers_are_rejected(moa):
         "moa_decode": lambda x: lib.moa_decode(plan._h, ok, ok, ok, 50, ok, x, 1 << 30, None),
         "moa_append_decode": lambda x: lib.moa_append_decode(plan._h, ok, ok, ok, x, ok, 50, ok, ok,
                                                              1 << 30, None),
+        "moa_append_decode_static": lambda x: lib.moa_append_decode_static(
+            plan._h, x, ok, ok, ok, ok, 50, ok, None),
     }
     for name, call in calls.items():
         assert call(bad) == moa.MOA_EINVAL, name
@@ -423,6 +425,30 @@ def test_host_only_plan_refuses_compute(moa):
                                  1 << 30, None) == moa.MOA_EINVAL
     assert "HOST_ONLY" in moa.last_error()
     plan.close()
+
+
+def test_static_decode_rejects_plan_beyond_scratch(moa):
+    """moa_append_decode_static refuses a plan whose partials exceed the fixed scratch, before
+    any device work and whatever the pointers (the size check needs no device)."""
+    lib = moa._lib
+    assert moa.static_workspace_bytes() == 16 << 20
+    # 2 KV heads of 65536 slots in 1024-slot chunks at batch 256: 32768 chunks of 520 bytes
+    big = moa.Plan(256, 2, 2, 128, 65536, [0, 0], [1.0, 1.0], host_only=True)
+    assert big.workspace_bytes > moa.static_workspace_bytes()
+    dummy = ctypes.c_void_p(16)   # never dereferenced
+    assert lib.moa_append_decode_static(big._h, dummy, dummy, dummy, dummy, dummy, 65536, dummy,
+                                        None) == moa.MOA_EWORKSPACE
+    assert "16777216" in moa.last_error() and "moa_append_decode_static" in moa.last_error()
+    # a plan that fits goes on to the ordinary checks (here: host-only plan)
+    small = moa.Plan(2, 2, 2, 128, 4096, [0, 0], [1.0, 1.0], host_only=True)
+    assert small.workspace_bytes <= moa.static_workspace_bytes()
+    assert lib.moa_append_decode_static(small._h, dummy, dummy, dummy, dummy, dummy, 4096, dummy,
+                                        None) == moa.MOA_EINVAL
+    assert "HOST_ONLY" in moa.last_error()
+    assert lib.moa_append_decode_static(None, dummy, dummy, dummy, dummy, dummy, 0, dummy,
+                                        None) == moa.MOA_EINVAL
+    big.close()
+    small.close()
 
 
 def test_error_message_is_thread_local(moa):
