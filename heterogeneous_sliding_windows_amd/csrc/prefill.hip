@@ -93,7 +93,9 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
   __shared__ __attribute__((aligned(16))) bf16 Vs[2][BN * D];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // wave-uniform, so that the LDS addresses of the tile loads are scalar
+  // arithmetic (no VALU write of an SGPR ahead of a load)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int half = lane >> 5;
