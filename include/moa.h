@@ -32,6 +32,11 @@
  *  - Threads: a plan is read-only after creation; distinct threads and
  *    streams may use one plan concurrently.  Calls that write the same cache
  *    or workspace must be ordered by the caller.
+ *  - HIP graphs: the compute calls only enqueue kernels (no allocation, copy
+ *    or memset), so they can be captured.  Positions (pos0, pos) reach the
+ *    kernels by value: a captured decode step appends and attends the same
+ *    position on every replay.  To advance, capture again or update the
+ *    captured kernel nodes' arguments (hipGraphExecKernelNodeSetParams).
  *  - Per-sequence prompt lengths (moa_plan_create_ragged): sequence b has a
  *    prompt of N_b <= N tokens, N = the longest.  Every [.., N, D] tensor
  *    keeps its shape; sequence b's prompt fills its last N_b rows (left

@@ -1,10 +1,12 @@
 """The hot calls inside HIP graphs: every replay must reproduce the eager calls bit for bit.
 
 The entry points only enqueue kernels on the caller's stream (no allocation, copy or
-memset), so a serving loop can capture them.  A fused prefill + ring handoff and a fused
-append + decode step are each captured once and replayed three times, with eager work
-(the outputs and rings cleared by fill kernels) and synchronisations between the replays;
-every replay's outputs and ring contents are checked.
+memset), so they can be captured.  A captured decode step is fixed to its position (pos is
+passed by value), so each replay here restores the rings and repeats the same step; a serving
+loop re-captures per position or updates the kernel nodes' arguments.  A fused prefill + ring
+handoff and a fused append + decode step are each captured once and replayed three times, with
+eager work (the outputs and rings cleared by fill kernels) and synchronisations between the
+replays; every replay's outputs and ring contents are checked.
 """
 
 import pytest
