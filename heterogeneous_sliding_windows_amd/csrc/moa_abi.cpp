@@ -14,10 +14,73 @@
 #include <cstring>
 #include <initializer_list>
 #include <new>
+#include <queue>
 #include <string>
 #include <vector>
 
 #include "moa_internal.h"
+
+namespace moa {
+
+namespace {
+
+// Chunks of `copies` sequences with rings `span` under cut c; INT64_MAX on overflow.
+int64_t count_chunks(const std::vector<int32_t>& span, int64_t copies, DecodeCut c) {
+  uint64_t one = 0;
+  for (const int32_t s : span) one += (uint64_t)cut_count(s, c);
+  uint64_t n;
+  if (__builtin_mul_overflow((uint64_t)copies, one, &n) || n > (uint64_t)INT64_MAX)
+    return INT64_MAX;
+  return (int64_t)n;
+}
+
+// The modeled end of a decode launch under cut c (the model DecodeCut states):
+// chunks in launch order, each on the resident slot that frees first.
+int64_t decode_makespan(const std::vector<int32_t>& span, int64_t copies, DecodeCut c,
+                        int slots) {
+  std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> free_at;
+  for (int i = 0; i < slots; ++i) free_at.push(0);
+  int64_t end = 0;
+  for (int64_t r = 0; r < copies; ++r)
+    for (const int32_t s : span) {
+      const int32_t step = cut_step(s, c);
+      for (int32_t first = 0; first < s; first += step) {
+        const int64_t t = free_at.top() + std::min(step, s - first) + kDecodeModelOverhead;
+        free_at.pop();
+        free_at.push(t);
+        end = std::max(end, t);
+      }
+    }
+  return end;
+}
+
+}  // namespace
+
+DecodeCut decode_cut(const std::vector<int32_t>& span, int64_t copies, int G, int D,
+                     int64_t* n_chunks) {
+  const int c = decode_chunk_for(G, [&](int cc) { return count_chunks(span, copies, {cc, false}); });
+  const DecodeCut fixed{c, false};
+  *n_chunks = count_chunks(span, copies, fixed);
+  const int slots = decode_resident(D);
+  if (*n_chunks >= kDecodeModelRounds * slots) return fixed;
+  const int64_t t_fixed = decode_makespan(span, copies, fixed, slots);
+  DecodeCut best = fixed;
+  int64_t t_best = INT64_MAX;
+  for (const int target : kDecodeEvenTargets) {
+    if (target < c) continue;
+    const DecodeCut even{target, true};
+    const int64_t t = decode_makespan(span, copies, even, slots);
+    if (t < t_best) {
+      t_best = t;
+      best = even;
+    }
+  }
+  if (!best.even || t_best * 100 > t_fixed * kDecodeModelGainPct) return fixed;
+  *n_chunks = count_chunks(span, copies, best);
+  return best;
+}
+
+}  // namespace moa
 
 namespace {
 
@@ -207,21 +270,22 @@ void build_prefill_items(moa_plan* p) {
 // Decode chunk list of all sequences: each ring's S slots cut into chunks of
 // at most decode_chunk slots, in (b, h) order.
 void build_decode_chunks(moa_plan* p) {
-  const int32_t c = p->decode_chunk;
+  const moa::DecodeCut cut{p->decode_chunk, p->decode_even};
   p->decode_chunks.clear();
   p->head_chunks.assign((size_t)p->B * p->Hkv * 2, 0);
   p->any_split = false;
   int64_t idx = 0;
   for (int32_t bh = 0; bh < p->B * p->Hkv; ++bh) {
     const int32_t s = p->span[bh];
-    const int32_t cnt = (s + c - 1) / c;
+    const int32_t step = moa::cut_step(s, cut);
+    const int32_t cnt = moa::cut_count(s, cut);
     p->any_split |= cnt > 1;
     p->head_chunks[2 * (size_t)bh + 0] = (int32_t)idx;
     p->head_chunks[2 * (size_t)bh + 1] = cnt;
     for (int32_t k = 0; k < cnt; ++k) {
       p->decode_chunks.push_back(bh);
-      p->decode_chunks.push_back(k * c);
-      p->decode_chunks.push_back(std::min(c, s - k * c));
+      p->decode_chunks.push_back(k * step);
+      p->decode_chunks.push_back(std::min(step, s - k * step));
       p->decode_chunks.push_back(cnt);
       ++idx;
     }
@@ -358,11 +422,10 @@ int create_plan(const moa_problem* pr, const int64_t* seq_len, uint32_t flags, m
     if (seq_len) std::copy(seq_len, seq_len + p->B, p->seq_len.begin());
     build_ring_tables(p, pr->alpha, pr->beta);
     build_prefill_items(p);
-    p->decode_chunk = moa::decode_chunk_for(p->G, [&](int c) {
-      int64_t n = 0;
-      for (const int32_t sp : p->span) n += (sp + c - 1) / c;
-      return n;
-    });
+    int64_t n_chunks = 0;
+    const moa::DecodeCut cut = moa::decode_cut(p->span, 1, p->G, p->D, &n_chunks);
+    p->decode_chunk = cut.size;
+    p->decode_even = cut.even;
     build_decode_chunks(p);
   } catch (const std::bad_alloc&) {
     delete p;
@@ -483,7 +546,7 @@ int64_t moa_max_batch(const moa_problem* pr, uint64_t budget_bytes) {
   // reports for batch B; the largest B with bytes(B) <= budget
   const uint64_t elem = p->dtype == MOA_BF16 ? 2 : 4;
   const uint64_t cache = 2ull * (uint64_t)p->total_slots * (uint64_t)p->D * elem;
-  const int G = p->G;
+  const int G = p->G, D = p->D;
   const uint64_t row = (uint64_t)G * ((uint64_t)p->D + 2) * 4ull;   // partial bytes per chunk
   const std::vector<int32_t> span = p->span;
   moa_plan_destroy(p);
@@ -496,14 +559,12 @@ int64_t moa_max_batch(const moa_problem* pr, uint64_t budget_bytes) {
   // bytes(b): both pools of b sequences plus the workspace a plan of batch b
   // would take; UINT64_MAX when that overflows (it cannot fit any budget)
   auto bytes = [&](uint64_t b) -> uint64_t {
-    const int c = moa::decode_chunk_for(G, [&](int cc) {
-      uint64_t n;
-      return __builtin_mul_overflow(b, per_seq(cc), &n) || n > (uint64_t)INT64_MAX
-                 ? INT64_MAX : (int64_t)n;
-    });
-    uint64_t pools, chunks, ws;
+    int64_t n_chunks = 0;
+    moa::decode_cut(span, (int64_t)b, G, D, &n_chunks);
+    if (n_chunks == INT64_MAX) return UINT64_MAX;
+    const uint64_t chunks = (uint64_t)n_chunks;
+    uint64_t pools, ws;
     if (__builtin_mul_overflow(b, cache, &pools) ||
-        __builtin_mul_overflow(b, per_seq(c), &chunks) ||
         __builtin_mul_overflow(chunks, row, &ws) || ws > UINT64_MAX - 511)
       return UINT64_MAX;
     ws = (ws + 255) & ~(uint64_t)255;

@@ -42,6 +42,57 @@ int decode_chunk_for(int G, F chunks_at) {
   return kDecodeChunk;
 }
 
+// How the rings are cut into decode chunks.  Fixed: chunks of `size` slots
+// from each ring's start, the last one shorter.  Even: a ring of s slots gets
+// ceil(s / size) chunks of one length, ceil(s / count) rounded up to a
+// multiple of 32 (the V pool's block), the last one shorter.
+struct DecodeCut {
+  int32_t size;
+  bool even;
+};
+// A plan whose fixed cut gives fewer than kDecodeModelRounds rounds of
+// resident workgroups ends on a partly filled last round, and there the cut
+// decides the launch time.  For such plans the planner models the launch:
+// workgroups start in chunk order, each on the first free slot of the
+// resident set, and hold it for their slot count plus kDecodeModelOverhead;
+// the launch ends with its last chunk.  Of the even cuts at the targets of
+// kDecodeEvenTargets no smaller than the fixed cut's size (so the even cut
+// never has more chunks, nor a larger workspace), it takes the one the model
+// finishes first (the smaller target on a tie), if that is no later than
+// kDecodeModelGainPct percent of the fixed cut's time; else the fixed cut.  (The model overstates a ragged last round about two to three times:
+// the workgroups still running there get more bandwidth each than the model
+// gives them, hence the margin.)
+constexpr int kDecodeEvenTargets[11] = {1024, 1536, 2048, 2560, 3072, 3584,
+                                        4096, 4608, 5120, 6144, 8192};
+constexpr int64_t kDecodeModelRounds = 8;
+constexpr int64_t kDecodeModelOverhead = 32;
+constexpr int64_t kDecodeModelGainPct = 92;
+// Decode workgroups resident per CU (256 threads each, one wave per SIMD):
+// the occupancy the compiled kernels reach, set by their register and LDS use.
+constexpr int kDecodeResidentD64 = 5;
+constexpr int kDecodeResidentD128 = 2;
+constexpr int kCUs = 256;
+inline int decode_resident(int D) {
+  return kCUs * (D == 128 ? kDecodeResidentD128 : kDecodeResidentD64);
+}
+// Chunk length of a ring of s slots under cut c (every chunk but the last).
+inline int32_t cut_step(int32_t s, DecodeCut c) {
+  if (!c.even || s <= 0) return c.size;
+  const int32_t n = (s + c.size - 1) / c.size;
+  const int32_t len = (s + n - 1) / n;
+  return (len + 31) / 32 * 32;
+}
+inline int32_t cut_count(int32_t s, DecodeCut c) {
+  if (s <= 0) return 0;
+  const int32_t step = cut_step(s, c);
+  return (s + step - 1) / step;
+}
+// The cut of `copies` sequences, each with the rings `span` (one sequence's,
+// or all of a plan's with copies = 1), for G query heads per KV head of
+// dimension D; *n_chunks receives its chunk count (INT64_MAX on overflow).
+DecodeCut decode_cut(const std::vector<int32_t>& span, int64_t copies, int G, int D,
+                     int64_t* n_chunks);
+
 struct PlanDevice {
   int32_t* span = nullptr;          // [B*Hkv] span of ring (b, h)
   int64_t* ring = nullptr;          // [B*Hkv] first slot of ring (b, h) in the pools
@@ -78,7 +129,8 @@ struct moa_plan {
   int64_t n_prefill_units = 0;            // units of all sequences
   std::vector<int32_t> decode_chunks;     // 4 per chunk, all sequences: {b*Hkv + h, first, n, chunks_of_ring}
   std::vector<int32_t> head_chunks;       // 2 per (b, h): {first chunk, count}
-  int32_t decode_chunk = moa::kDecodeChunk;
+  int32_t decode_chunk = moa::kDecodeChunk;   // longest chunk the cut allows
+  bool decode_even = false;               // even cut (else fixed)
   int64_t n_chunks = 0;                   // decode chunks of all sequences
   bool any_split = false;                 // some ring has more than one chunk
   moa::PlanDevice dev;

@@ -180,7 +180,10 @@ size_t moa_decode_workspace_bytes(moa_plan_t plan);
  * (>= 0, at most INT32_MAX: a plan's batch is int32) or a negative
  * moa_status (the problem is validated as by moa_plan_create).  Any budget
  * up to UINT64_MAX is accepted; byte counts that would overflow 64 bits count
- * as not fitting. */
+ * as not fitting.  The workspace follows the decode cut (moa_plan_decode_
+ * chunks), which can shrink it as the batch grows, so bytes(B) is not
+ * strictly monotone; the batch returned satisfies bytes(B) <= budget <
+ * bytes(B + 1), searched from budget / (bytes of one sequence). */
 int64_t moa_max_batch(const moa_problem* problem, uint64_t budget_bytes);
 
 /* Work-list inspection, for tests.  Prefill items are int32 sextuples
@@ -202,10 +205,22 @@ int64_t moa_max_batch(const moa_problem* problem, uint64_t budget_bytes);
  * entries, padding included, a multiple of 8) and runs that table once per
  * sequence: sequence b's unit at entry e runs in workgroup b*T + e.
  * Decode chunks are int32 quadruples {b, h_kv, first_slot, n_slots} of all
- * sequences, in launch order; each ring is cut into chunks of at most
- * moa_plan_decode_chunk() slots: 1024 when G = 1, else the largest of 3072,
- * 2048, 1536 that still gives the plan at least 2048 chunks (1024 if none
- * does).  Pass out = NULL to get the count; the
+ * sequences, in launch order (rings in (b, h_kv) order, each ring's chunks
+ * from its first slot); every chunk starts at a multiple of 32 slots and
+ * holds at most moa_plan_decode_chunk() = c slots.  The fixed cut takes c =
+ * 1024 when G = 1, else the largest of 3072, 2048, 1536 that still gives the
+ * plan at least 2048 chunks (1024 if none does), and cuts each ring into
+ * chunks of c slots, the last one shorter.  A plan whose fixed cut has fewer
+ * than 8 * R chunks (R = resident decode workgroups: 512 for D = 128, 1280
+ * for D = 64) may take an even cut instead: a ring of s slots gets
+ * ceil(s / c) chunks of ceil(s / ceil(s / c)) slots rounded up to a multiple
+ * of 32, the last one shorter.  The planner models a launch as chunks taken
+ * in order, each by the first of R slots to free, which it holds for n_slots
+ * + 32; of the even cuts at c in {1024, 1536, 2048, 2560, 3072, 3584, 4096,
+ * 4608, 5120, 6144, 8192}, c no smaller than the fixed cut's, it takes the
+ * one whose modeled end is earliest (the smaller c on a tie) if that end is
+ * at most 92% of the fixed cut's, else the fixed cut.  An even cut never has
+ * more chunks than the fixed cut.  Pass out = NULL to get the count; the
  * return value is the item count (>= 0) or a negative moa_status. */
 int64_t moa_plan_prefill_items(moa_plan_t plan, int32_t* out);
 int64_t moa_plan_decode_chunks(moa_plan_t plan, int32_t* out);

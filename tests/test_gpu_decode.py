@@ -158,9 +158,14 @@ def test_decode_full_size_every_head(moa, name):
     plan = moa.Plan(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, alpha, beta)
     lay = Layout(alpha, beta, w.batch, w.head_dim, w.n_prompt)
     assert plan.cache_elems == lay.total_slots * w.head_dim
-    log(f"{name}: decode chunk {plan.decode_chunk} slots, {len(plan.decode_chunks())} chunks")
+    ch = plan.decode_chunks()
+    even = bool(np.any((ch[:, 3] != plan.decode_chunk) & (ch[:, 2] + ch[:, 3] < lay.spans[ch[:, 1]])))
+    log(f"{name}: decode chunk {plan.decode_chunk} slots ({'even' if even else 'fixed'} cut), "
+        f"{len(ch)} chunks")
     if name == "gqa_chunk3072":
-        assert plan.decode_chunk == 3072
+        assert plan.decode_chunk == 3072 and not even
+    if name == "c4_decode":             # the even cut at full size (4448..4608-slot chunks)
+        assert plan.decode_chunk == 4608 and even
     log(f"{name}: filling {2 * plan.cache_elems * 2 / 1e9:.2f} GB of rings")
     kc = workloads.device_normal_(torch.empty(plan.cache_elems, dtype=torch.bfloat16,
                                               device="cuda"), 81)

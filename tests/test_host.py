@@ -7,6 +7,7 @@ must be rejected with the documented status before any device work.
 """
 
 import ctypes
+import heapq
 import os
 import re
 
@@ -233,21 +234,78 @@ def test_prefill_items_full_size_tables(moa):
         plan.close()
 
 
-@pytest.mark.parametrize("batch,hq,hkv,n", [
-    (64, 32, 32, 16384), (16, 64, 8, 65536), (8, 64, 8, 65536), (64, 256, 32, 16384),
-    (1, 8, 2, 1000), (2000, 8, 1, 4096)])
-def test_decode_chunk_rule(moa, batch, hq, hkv, n):
-    """1024 slots for ungrouped heads; with G > 1 the largest of 3072, 2048, 1536 that leaves
-    at least 2048 chunks, else 1024 (the rule include/moa.h states)."""
+def _cut_step(s, c, even):
+    """Chunk length of a ring of s slots: c for the fixed cut; for the even cut, the ring's
+    ceil(s / c) chunks share ceil(s / count) slots rounded up to a multiple of 32."""
+    if not even:
+        return c
+    n = -(-s // c)
+    return -(-(-(-s // n)) // 32) * 32
+
+
+def _decode_cut(spans, g, d):
+    """The decode cut include/moa.h states, restated: (chunk size, even) for a plan whose rings
+    have these spans in launch order, g query heads per KV head, head dimension d."""
+    def count(c, even):
+        return sum(-(-int(s) // _cut_step(int(s), c, even)) for s in spans)
+
+    def makespan(c, even, slots):
+        free = [0] * slots           # when each resident workgroup slot frees
+        end = 0
+        for s in spans:
+            s = int(s)
+            st = _cut_step(s, c, even)
+            for first in range(0, s, st):
+                t = heapq.heappop(free) + min(st, s - first) + 32
+                heapq.heappush(free, t)
+                end = max(end, t)
+        return end
+
+    c = 1024
+    if g > 1:
+        c = next((x for x in (3072, 2048, 1536) if count(x, False) >= 2048), 1024)
+    slots = 256 * (2 if d == 128 else 5)
+    if count(c, False) >= 8 * slots:
+        return c, False
+    t_fixed = makespan(c, False, slots)
+    best = min((makespan(t, True, slots), t) for t in
+               (1024, 1536, 2048, 2560, 3072, 3584, 4096, 4608, 5120, 6144, 8192) if t >= c)
+    return (best[1], True) if best[0] * 100 <= t_fixed * 92 else (c, False)
+
+
+def _cut_table(spans, hkv, c, even):
+    """{b, h, first, n} of every chunk, rings in (b, h) order."""
+    rows = []
+    for i, s in enumerate(int(x) for x in spans):
+        st = _cut_step(s, c, even)
+        rows += [(i // hkv, i % hkv, f, min(st, s - f)) for f in range(0, s, st)]
+    return np.array(rows, dtype=np.int32).reshape(-1, 4)
+
+
+@pytest.mark.parametrize("batch,hq,hkv,d,n,cut", [
+    (64, 32, 32, 128, 16384, (1024, False)), (16, 64, 8, 128, 65536, (4608, True)),
+    (8, 64, 8, 128, 65536, (4608, True)), (4, 64, 8, 128, 65536, (2560, True)),
+    (32, 64, 8, 128, 65536, (3072, False)), (64, 256, 32, 128, 16384, None),
+    (1, 8, 2, 128, 1000, None), (2000, 8, 1, 128, 4096, (3072, True)),
+    (3, 8, 2, 64, 20000, None), (40, 16, 2, 64, 30000, None), (2, 40, 40, 128, 32768, None)])
+def test_decode_chunk_rule(moa, batch, hq, hkv, d, n, cut):
+    """The fixed cut (1024 slots for ungrouped heads; with G > 1 the largest of 3072, 2048, 1536
+    that leaves at least 2048 chunks, else 1024), replaced by an even cut where the dispatch
+    model include/moa.h states finishes at least 8% sooner; the chunk table is rebuilt from
+    the rule.  `cut` pins the outcome where it is known (the 64-head 64k rules at batch 4 to
+    32, the 32-head 16k rules at batch 64)."""
     alpha, beta = workloads.rules("c4_decode")
     alpha, beta = (list(alpha) * 8)[:hkv], (list(beta) * 8)[:hkv]
-    plan = moa.Plan(batch, hq, hkv, 128, n, alpha, beta, host_only=True)
+    plan = moa.Plan(batch, hq, hkv, d, n, alpha, beta, host_only=True)
     s = np.tile(oracle.spans(alpha, beta, n), batch)
-    want = 1024
-    if hq // hkv > 1:
-        want = next((c for c in (3072, 2048, 1536) if int(np.sum((s + c - 1) // c)) >= 2048), 1024)
-    assert plan.decode_chunk == want
-    assert len(plan.decode_chunks()) == int(np.sum((s + want - 1) // want))
+    c, even = _decode_cut(s, hq // hkv, d)
+    if cut is not None:
+        assert (c, even) == cut
+    assert plan.decode_chunk == c
+    ch = plan.decode_chunks()
+    assert len(ch) == int(np.sum((s + c - 1) // c))
+    assert np.array_equal(ch, _cut_table(s, hkv, c, even))
+    _check_chunks(plan, ch)
     plan.close()
 
 
@@ -276,7 +334,7 @@ def _check_chunks(plan, ch):
             assert len(mine) == -(-s // c)
             covered = np.zeros(s, dtype=int)
             for _, _, first, cnt in mine:
-                assert 1 <= cnt <= c
+                assert 1 <= cnt <= c and first % 32 == 0
                 covered[first:first + cnt] += 1
             assert (covered == 1).all()
 
