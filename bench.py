@@ -304,6 +304,9 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times (the "
                          "known-size kernel that scales the HBM byte counters)")
+    ap.add_argument("--prealloc-gb", type=float, default=0.0, metavar="GB",
+                    help="allocate, fill and free GB of device memory before the legs, so the "
+                         "rings land where a process that allocates late would put them")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): heads and sequences "
@@ -327,6 +330,13 @@ def main():
     import heterogeneous_sliding_windows_amd as moa
     import workloads
 
+    if args.prealloc_gb > 0:
+        log(f"allocating, filling and freeing {args.prealloc_gb:g} GB before the legs")
+        big = torch.empty(int(args.prealloc_gb * 2**30), dtype=torch.uint8, device="cuda")
+        big.fill_(1)
+        torch.cuda.synchronize()
+        del big
+        torch.cuda.empty_cache()
     log(f"decode workload {args.workload}: warmup {args.warmup}, steps {args.steps}")
     dres = run_decode(moa, workloads, torch, args.workload, args.steps, args.warmup)
     plan, w = dres["plan"], dres["w"]
@@ -363,7 +373,8 @@ def main():
                    "head_dim": w.head_dim, "n_prompt": w.n_prompt,
                    "mean_density": round(float(np.mean(plan.spans)) / w.n_prompt, 4),
                    "step": "moa_append_decode: append of 1 token/seq fused into decode, "
-                           "one layer"},
+                           "one layer",
+                   **({"prealloc_gb": args.prealloc_gb} if args.prealloc_gb > 0 else {})},
         "hbm": {"step_GBps": round(step_bytes / (ms_step / 1e3) / 1e9, 1),
                 "step_frac": round(step_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
                 "bytes_per_step": step_bytes},

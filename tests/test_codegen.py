@@ -3,7 +3,7 @@ assembly generated from the kernel sources (no GPU needed; skipped without hipcc
 
 The compiler's hazard recognizer does not look inside assembly blocks, and it does not know
 what an assembly block is: a block's own instruction gets no wait states from it, and neither
-does a compiled instruction that follows a block.  The kernels have four kinds of block:
+does a compiled instruction that follows a block.  The kernels have two kinds of block:
 
 * LDS-direct tile loads (buffer_load_dwordx4 ... lds).  A vector memory instruction that reads
   an SGPR written by a VALU instruction (v_readlane, v_readfirstlane, ...) needs five wait states
@@ -14,20 +14,20 @@ does a compiled instruction that follows a block.  The kernels have four kinds o
   the schedule the build uses (the default machine scheduler).  Under iterative-ilp the
   compiler reloads resource words from spill lanes (v_readlane) right before the loads, which
   would need the five: the scan finds those, and that schedule is not used.
-* The prefill's Q.K matrix products, written as assembly so that their results stay in VGPRs
-  (see prefill.hip).  The CDNA3 ISA reference's table of independent instructions required
-  between matrix (MAI) instructions and their dependents ("Dependency Resolution: Required
-  Independent Instructions") sets two waits: a VALU write of a register (v_accvgpr_write and
-  v_accvgpr_mov included) before a matrix product reads it as a source, and a matrix product's
-  result before a vector instruction touches it.  The numbers used are the ones this compiler
-  inserts for the same dependences between builtins on gfx950: 2 wait states for the first, and
-  12 after a 32x32x16 product (8 after a 16x16x32 one) for the second (a dependent product that reads the result as its
-  accumulator issues back to back, as the same table allows).
-* The prefill's rescale moves (v_accvgpr_read / v_accvgpr_write of O around the P.V products),
-  held to the same two rules.
 * v_permlane32_swap / v_permlane16_swap row exchanges (written as assembly because the builtin's
   two results were merged): 2 wait states after a VALU write of either operand, the wait this
   compiler inserts before the builtin.
+
+The matrix products (v_mfma_*) are compiler builtins, so the compiler places their waits; the
+scan holds them to the rules of the CDNA3 ISA reference's table of independent instructions
+required between matrix (MAI) instructions and their dependents ("Dependency Resolution:
+Required Independent Instructions") all the same, which guards against a product or an
+accumulator move written as assembly later: a VALU write of a register (v_accvgpr_write and
+v_accvgpr_mov included) needs 2 wait states before a matrix product reads it as a source, and a
+matrix product's result needs 12 after a 32x32x16 product (8 after a 16x16x32 one) before a
+vector instruction touches it (the numbers this compiler inserts for the same dependences on
+gfx950; a dependent product that reads the result as its accumulator issues back to back, as
+the same table allows).
 
 The sources are compiled with the build's flags under the default machine scheduler and under
 iterative-ilp; the scan counts wait states as s_nop N = N + 1 and any other instruction 1, along
