@@ -41,6 +41,7 @@ sys.path.insert(0, ROOT)
 METRIC = ("decode attn tokens/s + HBM GB/s % peak; prefill TFLOP/s % MFMA peak")
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
+MFMA_F32_PEAK_TFLOPS = 157.3    # MI355X dense fp32 matrix cores
 DECODE_COUNTERS = os.path.join(ROOT, "profiles", "decode_c2_counters.json")
 PREFILL_COUNTERS = os.path.join(ROOT, "profiles", "prefill_c1_counters.json")
 
@@ -194,13 +195,15 @@ def run_prefill(moa, workloads, torch, name, iters, warmup, dense=False):
     alpha, beta = workloads.rules(name)
     if dense:   # every head keeps the whole prompt: full causal attention
         alpha, beta = [w.n_prompt] * w.n_kv_heads, [0.0] * w.n_kv_heads
-    plan = moa.Plan(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, alpha, beta)
+    plan = moa.Plan(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, alpha, beta,
+                    dtype=w.dtype)
     dev = torch.device("cuda")
+    tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
     shp_q = (w.batch, w.n_q_heads, w.n_prompt, w.head_dim)
     shp_kv = (w.batch, w.n_kv_heads, w.n_prompt, w.head_dim)
-    q = workloads.device_normal_(torch.empty(shp_q, dtype=torch.bfloat16, device=dev), 21)
-    k = workloads.device_normal_(torch.empty(shp_kv, dtype=torch.bfloat16, device=dev), 22)
-    v = workloads.device_normal_(torch.empty(shp_kv, dtype=torch.bfloat16, device=dev), 23)
+    q = workloads.device_normal_(torch.empty(shp_q, dtype=tdt, device=dev), 21)
+    k = workloads.device_normal_(torch.empty(shp_kv, dtype=tdt, device=dev), 22)
+    v = workloads.device_normal_(torch.empty(shp_kv, dtype=tdt, device=dev), 23)
     o = torch.empty_like(q)
     kc, vc = plan.new_cache()
     stream = torch.cuda.current_stream()
@@ -421,6 +424,8 @@ def main():
         pplan, pw = pres["plan"], pres["w"]
         fl = prefill_flops(pplan)
         tf = fl / (pres["ms"] / 1e3) / 1e12
+        f32 = pw.dtype == "f32"
+        peak = MFMA_F32_PEAK_TFLOPS if f32 else MFMA_BF16_PEAK_TFLOPS
         log(f"prefill: {pres['ms']:.3f} ms, {tf:.1f} TFLOP/s, handoff {pres['handoff_ms']:.3f} ms;"
             f" fused prefill+handoff {pres['fused_ms']:.3f} ms")
         line["prefill"] = {
@@ -428,12 +433,12 @@ def main():
             "tflops": round(tf, 2), "handoff_ms": round(pres["handoff_ms"], 4),
             "fused_prefill_handoff_ms": round(pres["fused_ms"], 4),
             "flops": fl,
-            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": peak,
+                         "unit": "TFLOP/s", "frac": round(tf / peak, 4),
                          "traffic": (counter_traffic(PREFILL_COUNTERS, "prefill.hip", "moa_device.h",
                                                      "moa_internal.h", "moa_abi.cpp")
                                      if pw.name == "c1_prefill" else None),
-                         "kernel": f"prefill_bf16_kernel<{pw.head_dim}>"},
+                         "kernel": f"prefill_{'f32' if f32 else 'bf16'}_kernel<{pw.head_dim}>"},
         }
         if not args.no_dense:
             pd = run_prefill(moa, workloads, torch, args.prefill_workload, args.prefill_iters, 3,

@@ -44,8 +44,9 @@
 //    by more than 8 in the exp2 domain (a factor of 2^8), which most tiles
 //    after the first never trigger.
 //
-// f32 kernel (the float32 dtype): 2 threads per query row, each owning half
-// of the head dimension; K/V tiles in LDS; plain FMA arithmetic.
+// f32 kernel (the float32 dtype): the same units and softmax on fp32 matrix
+// cores (v_mfma_f32_16x16x4f32), K/V tiles in LDS, an exact running max (no
+// lazy rescale).
 //
 // Fused handoff (RING = true): besides o, the launch writes positions
 // N - S_h .. N - 1 of every (b, h_kv) into the KV rings, as an append of the
@@ -393,6 +394,20 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
   }
 }
 
+// f32 kernel: 4 waves of 32 query rows (two 16-row blocks qb), both products
+// on v_mfma_f32_16x16x4f32 (A 16x4: lane l gives row l%16, k l/16; B 4x16:
+// lane l gives k l/16, column l%16; C 16x16: lane l holds rows 4*(l/16)+r,
+// column l%16).  S^T = K Q^T puts the query on the column, so lane l owns
+// query 16qb + l%16 and holds keys 16kb + 4*(l/16) + r of key block kb: the
+// row max and row sum are in-lane plus two exchanges across the lane groups,
+// and the P^T operand of O^T = V^T P^T is the lane's own weight (step (kb,
+// r) contracts keys 16kb + 4g + r, g = 0..3).  Each contraction may take its
+// index in any order, so the dimensions are permuted to make every operand
+// read a 16-byte one: Q.K step s pairs lane group g with dimension g*(D/4) +
+// s, and output block db holds dimensions i*(D/16) + db in row i.  K and V
+// tiles sit in LDS with each row's 16-byte chunks rotated by the key (chunk c
+// of key r at (c + r) mod (D/4)), so the 16 rows (or 16 chunks) a read phase
+// meets fall in different banks.
 template <int D, bool RING>
 __global__ __launch_bounds__(256) void prefill_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
@@ -400,11 +415,15 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
     const int32_t* __restrict__ seq_len, int seq_grid, int Hq, int Hkv, int G, int Npad,
     float scale_log2, float* __restrict__ kc, float* __restrict__ vc,
     const int64_t* __restrict__ ring) {
-  constexpr int DH = D / 2;
-  __shared__ __attribute__((aligned(16))) float Ks[BN * D];
-  __shared__ __attribute__((aligned(16))) float Vs[BN * D];
+  constexpr int C4 = D / 4;    // 16-byte chunks per K/V row; also the Q.K k-steps
+  constexpr int DB = D / 16;   // 16-dim output blocks
+  __shared__ float4 Ks[BN * C4];
+  __shared__ float4 Vs[BN * C4];
   const int tid = threadIdx.x;
-  const int half = tid & 1;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int j = lane & 15;     // query column (S^T, O^T) / key or dim row (operands)
+  const int g = lane >> 4;     // lane group
   // the table runs once per sequence (seq_grid > 0) or names the sequence
   const unsigned copy = seq_grid > 0 ? blockIdx.x / (unsigned)seq_grid : 0u;
   const int4 it = items[blockIdx.x - copy * (unsigned)seq_grid];
@@ -418,7 +437,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
   const int64_t pad = Npad - N;
   const float* kb = k + (((int64_t)b * Hkv + hkv) * Npad + pad) * D;
   const float* vb = v + (((int64_t)b * Hkv + hkv) * Npad + pad) * D;
-  const int my_q = qt * BM + (tid >> 1);
+  const int iw0 = qt * BM + wave * 32;   // first query row of this wave
   // fused handoff (see the file comment): only g = 0 writes the rings
   float* kring = nullptr;
   float* vring = nullptr;
@@ -430,36 +449,44 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
     }
   }
 
-  float qr[DH];
-  const float* qrow = q + ((int64_t)bh * Npad + pad + (my_q < N ? my_q : 0)) * D + half * DH;
+  // B operand of Q.K step s: Q[query 16qb + j][dim g*C4 + s], loaded once
+  float qv[2][C4];
 #pragma unroll
-  for (int e = 0; e < DH; e += 4) {
-    const float4 x = *reinterpret_cast<const float4*>(qrow + e);
-    qr[e] = x.x; qr[e + 1] = x.y; qr[e + 2] = x.z; qr[e + 3] = x.w;
+  for (int qb = 0; qb < 2; ++qb) {
+    const int row = iw0 + 16 * qb + j;
+    const float* qrow = q + ((int64_t)bh * Npad + pad + (row < N ? row : 0)) * D + g * C4;
+#pragma unroll
+    for (int c = 0; c < C4; c += 4) {
+      const float4 x = row < N ? *reinterpret_cast<const float4*>(qrow + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+      qv[qb][c] = x.x; qv[qb][c + 1] = x.y; qv[qb][c + 2] = x.z; qv[qb][c + 3] = x.w;
+    }
   }
-  float acc[DH];
+  floatx4 acc[2][DB];
 #pragma unroll
-  for (int e = 0; e < DH; ++e) acc[e] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int d = 0; d < DB; ++d) acc[qb][d] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_part[2] = {0.f, 0.f};   // this lane's keys; the row sum adds the 4 lane groups
 
   for (int kt = kt_lo; kt <= kt_hi; ++kt) {
     const int j0 = kt * BN;
     __syncthreads();
-    for (int i = tid; i < BN * D / 4; i += 256) {
-      const int key = j0 + (i * 4) / D;
+    for (int i = tid; i < BN * C4; i += 256) {
+      const int r = i / C4, c = i % C4;
+      const int key = j0 + r;
       float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
       if (key < N) {
-        kx = *reinterpret_cast<const float4*>(kb + (int64_t)j0 * D + 4 * i);
-        vx = *reinterpret_cast<const float4*>(vb + (int64_t)j0 * D + 4 * i);
+        kx = *reinterpret_cast<const float4*>(kb + (int64_t)key * D + 4 * c);
+        vx = *reinterpret_cast<const float4*>(vb + (int64_t)key * D + 4 * c);
       }
-      *reinterpret_cast<float4*>(&Ks[4 * i]) = kx;
-      *reinterpret_cast<float4*>(&Vs[4 * i]) = vx;
+      Ks[r * C4 + (c + r) % C4] = kx;
+      Vs[r * C4 + (c + r) % C4] = vx;
       if constexpr (RING) {
         if (kring != nullptr && kt * BN / BM == qt && key >= N - S && key < N) {
           const int slot = key % S;
-          const int d = (4 * i) % D;
-          *reinterpret_cast<float4*>(kring + (int64_t)slot * D + d) = kx;
-          float* dst = vring + (int64_t)(slot >> 5) * (32 * D) + d * 32 + (slot & 31);
+          *reinterpret_cast<float4*>(kring + (int64_t)slot * D + 4 * c) = kx;
+          float* dst = vring + (int64_t)(slot >> 5) * (32 * D) + 4 * c * 32 + (slot & 31);
           dst[0] = vx.x;
           dst[32] = vx.y;
           dst[64] = vx.z;
@@ -468,44 +495,99 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
       }
     }
     __syncthreads();
-    float sc[BN];
-    float mx = -INFINITY;
+
+    // S^T blocks: st[qb][kb][r] = score of query iw0 + 16qb + j, key j0 + 16kb + 4g + r
+    floatx4 st[2][4];
 #pragma unroll
-    for (int j = 0; j < BN; ++j) {
-      const float* kr = &Ks[j * D + half * DH];
-      float s = 0.f;
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int e = 0; e < DH; ++e) s = __builtin_fmaf(qr[e], kr[e], s);
-      s += __shfl_xor(s, 1, 64);
-      const int key = j0 + j;
-      const bool ok = key <= my_q && key >= my_q - S + 1 && key < N;
-      sc[j] = ok ? s : -INFINITY;
-      mx = fmaxf(mx, sc[j]);
+      for (int kb2 = 0; kb2 < 4; ++kb2) st[qb][kb2] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb2 = 0; kb2 < 4; ++kb2) {
+      const int r = 16 * kb2 + j;   // A row: key r of the tile
+#pragma unroll
+      for (int c = 0; c < C4 / 4; ++c) {
+        const float4 kf = Ks[r * C4 + (g * (C4 / 4) + c + r) % C4];   // dims g*C4 + 4c .. +3
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          st[qb][kb2] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.x, qv[qb][4 * c + 0], st[qb][kb2], 0, 0, 0);
+          st[qb][kb2] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.y, qv[qb][4 * c + 1], st[qb][kb2], 0, 0, 0);
+          st[qb][kb2] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.z, qv[qb][4 * c + 2], st[qb][kb2], 0, 0, 0);
+          st[qb][kb2] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.w, qv[qb][4 * c + 3], st[qb][kb2], 0, 0, 0);
+        }
+      }
     }
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2((m_run - m_use) * scale_log2);
-    m_run = m_new;
-    l_run *= alpha;
+    // online softmax per row (fp32, exact running max; masked scores -> weight 0)
 #pragma unroll
-    for (int e = 0; e < DH; ++e) acc[e] *= alpha;
+    for (int qb = 0; qb < 2; ++qb) {
+      const int my_q = iw0 + 16 * qb + j;
+      float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < BN; ++j) {
-      // (s - m) first: a score equal to the running max gives exactly 1
-      const float p = exp2f((sc[j] - m_use) * scale_log2);
-      l_run += p;
-      const float* vr = &Vs[j * D + half * DH];
+      for (int kb2 = 0; kb2 < 4; ++kb2)
 #pragma unroll
-      for (int e = 0; e < DH; ++e) acc[e] = __builtin_fmaf(p, vr[e], acc[e]);
+        for (int r = 0; r < 4; ++r) {
+          const int key = j0 + 16 * kb2 + 4 * g + r;
+          const bool ok = key <= my_q && key >= my_q - S + 1 && key < N;
+          st[qb][kb2][r] = ok ? st[qb][kb2][r] : -INFINITY;
+          mx = fmaxf(mx, st[qb][kb2][r]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run[qb], mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2((m_run[qb] - m_use) * scale_log2);
+      m_run[qb] = m_new;
+      float ls = 0.f;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 4; ++kb2)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          // (s - m) first: a score equal to the running max gives exactly 1
+          const float pw = exp2f((st[qb][kb2][r] - m_use) * scale_log2);
+          st[qb][kb2][r] = pw;
+          ls += pw;
+        }
+      l_part[qb] = l_part[qb] * alpha + ls;
+#pragma unroll
+      for (int d = 0; d < DB; ++d) acc[qb][d] *= alpha;
     }
+    // O^T += V^T P^T, step (kb, r): keys 16kb + 4g + r; A = V[key][dim j*DB + db]
+#pragma unroll
+    for (int kb2 = 0; kb2 < 4; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = 16 * kb2 + 4 * g + r;
+        float va[DB];
+#pragma unroll
+        for (int u = 0; u < DB / 4; ++u) {
+          const float4 x = Vs[key * C4 + (j * (DB / 4) + u + key) % C4];   // dims j*DB + 4u .. +3
+          va[4 * u] = x.x; va[4 * u + 1] = x.y; va[4 * u + 2] = x.z; va[4 * u + 3] = x.w;
+        }
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int d = 0; d < DB; ++d)
+            acc[qb][d] = __builtin_amdgcn_mfma_f32_16x16x4f32(va[d], st[qb][kb2][r], acc[qb][d], 0, 0, 0);
+      }
   }
-  if (my_q >= N) return;
-  const float inv = 1.f / l_run;
-  float* orow = o + ((int64_t)bh * Npad + pad + my_q) * D + half * DH;
+  // acc[qb][db][r'] = O[query iw0 + 16qb + j][dim (4g + r')*DB + db]
 #pragma unroll
-  for (int e = 0; e < DH; e += 4)
-    *reinterpret_cast<float4*>(orow + e) =
-        make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv);
+  for (int qb = 0; qb < 2; ++qb) {
+    float l = l_part[qb];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const int my_q = iw0 + 16 * qb + j;
+    if (my_q >= N) continue;
+    const float inv = 1.f / l;
+    float* orow = o + ((int64_t)bh * Npad + pad + my_q) * D;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int u = 0; u < DB / 4; ++u)
+        *reinterpret_cast<float4*>(orow + (4 * g + r) * DB + 4 * u) =
+            make_float4(acc[qb][4 * u][r] * inv, acc[qb][4 * u + 1][r] * inv,
+                        acc[qb][4 * u + 2][r] * inv, acc[qb][4 * u + 3][r] * inv);
+  }
 }
 
 template <int D, bool RING>

@@ -24,7 +24,7 @@ required between matrix (MAI) instructions and their dependents ("Dependency Res
 Required Independent Instructions") all the same, which guards against a product or an
 accumulator move written as assembly later: a VALU write of a register (v_accvgpr_write and
 v_accvgpr_mov included) needs 2 wait states before a matrix product reads it as a source, and a
-matrix product's result needs 12 after a 32x32x16 product (8 after a 16x16x32 one) before a
+matrix product's result needs 12 after a 32x32x16 product (8 after a 16x16 one) before a
 vector instruction touches it (the numbers this compiler inserts for the same dependences on
 gfx950; a dependent product that reads the result as its accumulator issues back to back, as
 the same table allows).
@@ -143,7 +143,8 @@ SWAP_SRC_WAIT = 2       # VALU write -> v_permlane*_swap operand
 
 def mai_result_wait(op):
     """Wait states after a matrix product before a vector instruction touches its result: 12 for
-    the 32x32x16 shape, 8 for 16x16x32 (the compiler's own waits for each on gfx950)."""
+    the 32x32x16 shape, 8 for the 16x16 ones (16x16x32 bf16, 16x16x4 f32): the compiler's own
+    waits for each on gfx950."""
     return 12 if "32x32" in op else 8
 
 
