@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
     const int64_t* __restrict__ ring_off, const int32_t* __restrict__ seq_len, int Npad, int Hq,
     int G, float scale_log2, bf16* __restrict__ o, float* __restrict__ ws_o,
     float2* __restrict__ ws_ml, const bf16* __restrict__ kn, const bf16* __restrict__ vn,
-    int64_t pos) {
+    int64_t pos, const int32_t* __restrict__ order) {
   constexpr int KS = D / 32;  // k-steps of the Q.K product
   constexpr int VT = D / 16;  // 16-dim tiles of the output
   __shared__ float sh_o[kWaves][D][17];
@@ -105,7 +105,8 @@ __global__ __launch_bounds__(256) void decode_kernel(
   const int col = lane & 15;   // query head within the group
   const int quad = lane >> 4;
 
-  const int part = blockIdx.x;       // chunk of all sequences' rings
+  // chunk of all sequences' rings; a plan may launch them in another order
+  const int part = order != nullptr ? order[blockIdx.x] : (int)blockIdx.x;
   const int4 ch = chunks[part];
   const int bh = ch.x, first = ch.y, len = ch.z, n_head_chunks = ch.w;
   const int Hkv = Hq / G;
@@ -421,7 +422,8 @@ hipError_t launch(const moa_plan& p, const void* q, const void* kc, const void* 
                      static_cast<const bf16*>(q), static_cast<const bf16*>(kc),
                      static_cast<const bf16*>(vc), p.dev.decode_chunks, p.dev.span, p.dev.ring,
                      p.dev.seq_len, (int)p.N, p.Hq, p.G, scale_log2, static_cast<bf16*>(o), w.o,
-                     w.ml, static_cast<const bf16*>(kn), static_cast<const bf16*>(vn), pos);
+                     w.ml, static_cast<const bf16*>(kn), static_cast<const bf16*>(vn), pos,
+                     p.dev.decode_order);
   hipError_t e = hipGetLastError();
   // the combine runs when some head is split, and always for a fused append
   // (it writes the new rows)

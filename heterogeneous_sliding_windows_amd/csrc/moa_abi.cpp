@@ -25,7 +25,7 @@ namespace moa {
 namespace {
 
 // Chunks of `copies` sequences with rings `span` under cut c; INT64_MAX on overflow.
-int64_t count_chunks(const std::vector<int32_t>& span, int64_t copies, DecodeCut c) {
+int64_t count_chunks(const std::vector<int32_t>& span, int64_t copies, const DecodeCut& c) {
   uint64_t one = 0;
   for (const int32_t s : span) one += (uint64_t)cut_count(s, c);
   uint64_t n;
@@ -36,7 +36,7 @@ int64_t count_chunks(const std::vector<int32_t>& span, int64_t copies, DecodeCut
 
 // The modeled end of a decode launch under cut c (the model DecodeCut states):
 // chunks in launch order, each on the resident slot that frees first.
-int64_t decode_makespan(const std::vector<int32_t>& span, int64_t copies, DecodeCut c,
+int64_t decode_makespan(const std::vector<int32_t>& span, int64_t copies, const DecodeCut& c,
                         int slots) {
   std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> free_at;
   for (int i = 0; i < slots; ++i) free_at.push(0);
@@ -58,26 +58,48 @@ int64_t decode_makespan(const std::vector<int32_t>& span, int64_t copies, Decode
 
 DecodeCut decode_cut(const std::vector<int32_t>& span, int64_t copies, int G, int D,
                      int64_t* n_chunks) {
-  const int c = decode_chunk_for(G, [&](int cc) { return count_chunks(span, copies, {cc, false}); });
-  const DecodeCut fixed{c, false};
+  const int c = decode_chunk_for(G, [&](int cc) {
+    return count_chunks(span, copies, {CutKind::kFixed, cc});
+  });
+  const DecodeCut fixed{CutKind::kFixed, c};
+  DecodeCut cut = fixed;
   *n_chunks = count_chunks(span, copies, fixed);
   const int slots = decode_resident(D);
-  if (*n_chunks >= kDecodeModelRounds * slots) return fixed;
-  const int64_t t_fixed = decode_makespan(span, copies, fixed, slots);
-  DecodeCut best = fixed;
-  int64_t t_best = INT64_MAX;
-  for (const int target : kDecodeEvenTargets) {
-    if (target < c) continue;
-    const DecodeCut even{target, true};
-    const int64_t t = decode_makespan(span, copies, even, slots);
-    if (t < t_best) {
-      t_best = t;
-      best = even;
+  if (*n_chunks < kDecodeModelRounds * slots) {
+    const int64_t t_fixed = decode_makespan(span, copies, fixed, slots);
+    DecodeCut best = fixed;
+    int64_t t_best = INT64_MAX;
+    for (const int target : kDecodeEvenTargets) {
+      if (target < c) continue;
+      const DecodeCut even{CutKind::kEven, target};
+      const int64_t t = decode_makespan(span, copies, even, slots);
+      if (t < t_best) {
+        t_best = t;
+        best = even;
+      }
+    }
+    if (best.kind == CutKind::kEven && t_best * 100 <= t_fixed * kDecodeModelGainPct) {
+      cut = best;
+      *n_chunks = count_chunks(span, copies, best);
     }
   }
-  if (!best.even || t_best * 100 > t_fixed * kDecodeModelGainPct) return fixed;
-  *n_chunks = count_chunks(span, copies, best);
-  return best;
+  uint64_t rings;
+  if (G > 1 && *n_chunks > slots && !__builtin_mul_overflow((uint64_t)copies, (uint64_t)span.size(), &rings) &&
+      rings <= (uint64_t)slots) {
+    int64_t total = 0;
+    for (const int32_t s : span) total += s;
+    total *= copies;   // rings <= slots, so at most 2^31 * 2^11
+    const int64_t cap = kDecodeBalancedRounds * slots;
+    for (int64_t k = cap; k >= (int64_t)rings; --k) {
+      const DecodeCut bal{CutKind::kBalanced, 0, k, total};
+      const int64_t n = count_chunks(span, copies, bal);
+      if (n <= cap) {
+        *n_chunks = n;
+        return bal;
+      }
+    }
+  }
+  return cut;
 }
 
 }  // namespace moa
@@ -150,6 +172,7 @@ void free_device(moa_plan* p) {
   hipFree(p->dev.prefill_items);
   hipFree(p->dev.decode_chunks);
   hipFree(p->dev.head_chunks);
+  hipFree(p->dev.decode_order);
   p->dev = moa::PlanDevice{};
 }
 
@@ -270,15 +293,17 @@ void build_prefill_items(moa_plan* p) {
 // Decode chunk list of all sequences: each ring's S slots cut into chunks of
 // at most decode_chunk slots, in (b, h) order.
 void build_decode_chunks(moa_plan* p) {
-  const moa::DecodeCut cut{p->decode_chunk, p->decode_even};
+  const moa::DecodeCut& cut = p->decode_cut;
   p->decode_chunks.clear();
   p->head_chunks.assign((size_t)p->B * p->Hkv * 2, 0);
   p->any_split = false;
+  int32_t longest = 0;
   int64_t idx = 0;
   for (int32_t bh = 0; bh < p->B * p->Hkv; ++bh) {
     const int32_t s = p->span[bh];
     const int32_t step = moa::cut_step(s, cut);
     const int32_t cnt = moa::cut_count(s, cut);
+    longest = std::max(longest, std::min(step, s));
     p->any_split |= cnt > 1;
     p->head_chunks[2 * (size_t)bh + 0] = (int32_t)idx;
     p->head_chunks[2 * (size_t)bh + 1] = cnt;
@@ -291,6 +316,18 @@ void build_decode_chunks(moa_plan* p) {
     }
   }
   p->n_chunks = idx;
+  // the size bound of the cut: fixed size or even target, else the longest chunk
+  p->decode_chunk = cut.kind == moa::CutKind::kBalanced ? longest : cut.size;
+  // the balanced cut launches its chunks longest first (stable: equal lengths
+  // keep the (b, h) order); the chunk table itself stays ring-contiguous
+  p->decode_order.clear();
+  if (cut.kind == moa::CutKind::kBalanced) {
+    p->decode_order.resize((size_t)idx);
+    for (int64_t i = 0; i < idx; ++i) p->decode_order[(size_t)i] = (int32_t)i;
+    std::stable_sort(p->decode_order.begin(), p->decode_order.end(), [&](int32_t a, int32_t b) {
+      return p->decode_chunks[4 * (size_t)a + 2] > p->decode_chunks[4 * (size_t)b + 2];
+    });
+  }
 }
 
 // Device pointers must be 16-byte aligned (include/moa.h): the kernels move
@@ -423,9 +460,7 @@ int create_plan(const moa_problem* pr, const int64_t* seq_len, uint32_t flags, m
     build_ring_tables(p, pr->alpha, pr->beta);
     build_prefill_items(p);
     int64_t n_chunks = 0;
-    const moa::DecodeCut cut = moa::decode_cut(p->span, 1, p->G, p->D, &n_chunks);
-    p->decode_chunk = cut.size;
-    p->decode_even = cut.even;
+    p->decode_cut = moa::decode_cut(p->span, 1, p->G, p->D, &n_chunks);
     build_decode_chunks(p);
   } catch (const std::bad_alloc&) {
     delete p;
@@ -449,7 +484,8 @@ int create_plan(const moa_problem* pr, const int64_t* seq_len, uint32_t flags, m
         (st = dev_upload(&p->dev.seq_len, lens)) != MOA_OK ||
         (st = dev_upload(&p->dev.prefill_items, items)) != MOA_OK ||
         (st = dev_upload(&p->dev.decode_chunks, chunks)) != MOA_OK ||
-        (st = dev_upload(&p->dev.head_chunks, hc)) != MOA_OK) {
+        (st = dev_upload(&p->dev.head_chunks, hc)) != MOA_OK ||
+        (st = dev_upload(&p->dev.decode_order, p->decode_order)) != MOA_OK) {
       free_device(p);
       delete p;
       return st;
@@ -610,12 +646,13 @@ int64_t moa_plan_decode_chunks(moa_plan_t p, int32_t* out) {
   if (st != MOA_OK) return st;
   const size_t n = p->decode_chunks.size() / 4;
   if (out)
-    for (size_t i = 0; i < n; ++i) {
-      const int32_t bh = p->decode_chunks[4 * i];
+    for (size_t i = 0; i < n; ++i) {   // in launch order
+      const size_t c = p->decode_order.empty() ? i : (size_t)p->decode_order[i];
+      const int32_t bh = p->decode_chunks[4 * c];
       out[4 * i + 0] = bh / p->Hkv;
       out[4 * i + 1] = bh % p->Hkv;
-      out[4 * i + 2] = p->decode_chunks[4 * i + 1];
-      out[4 * i + 3] = p->decode_chunks[4 * i + 2];
+      out[4 * i + 2] = p->decode_chunks[4 * c + 1];
+      out[4 * i + 3] = p->decode_chunks[4 * c + 2];
     }
   return (int64_t)n;
 }

@@ -45,10 +45,16 @@ int decode_chunk_for(int G, F chunks_at) {
 // How the rings are cut into decode chunks.  Fixed: chunks of `size` slots
 // from each ring's start, the last one shorter.  Even: a ring of s slots gets
 // ceil(s / size) chunks of one length, ceil(s / count) rounded up to a
-// multiple of 32 (the V pool's block), the last one shorter.
+// multiple of 32 (the V pool's block), the last one shorter.  Balanced: a
+// ring gets n = max(1, floor((s * k + total / 2) / total)) chunks of one
+// length, ceil(s / n) rounded up to 32, where total is the slots of all the
+// plan's rings: every chunk of the plan about total / k slots long.
+enum class CutKind { kFixed, kEven, kBalanced };
 struct DecodeCut {
-  int32_t size;
-  bool even;
+  CutKind kind;
+  int32_t size;       // fixed: chunk slots; even: target slots; balanced: 0
+  int64_t k = 0;      // balanced: the chunk count the split aims at
+  int64_t total = 0;  // balanced: slots of all rings
 };
 // A plan whose fixed cut gives fewer than kDecodeModelRounds rounds of
 // resident workgroups ends on a partly filled last round, and there the cut
@@ -59,14 +65,23 @@ struct DecodeCut {
 // kDecodeEvenTargets no smaller than the fixed cut's size (so the even cut
 // never has more chunks, nor a larger workspace), it takes the one the model
 // finishes first (the smaller target on a tie), if that is no later than
-// kDecodeModelGainPct percent of the fixed cut's time; else the fixed cut.  (The model overstates a ragged last round about two to three times:
-// the workgroups still running there get more bandwidth each than the model
-// gives them, hence the margin.)
+// kDecodeModelGainPct percent of the fixed cut's time; else the fixed cut.
+// (The model overstates a ragged last round about two to three times: the
+// workgroups still running there get more bandwidth each than the model gives
+// them, hence the margin.)
 constexpr int kDecodeEvenTargets[11] = {1024, 1536, 2048, 2560, 3072, 3584,
                                         4096, 4608, 5120, 6144, 8192};
 constexpr int64_t kDecodeModelRounds = 8;
 constexpr int64_t kDecodeModelOverhead = 32;
 constexpr int64_t kDecodeModelGainPct = 92;
+// Grouped heads (G > 1) whose cut so far still takes more than one round of
+// resident workgroups, in plans of at most one round of rings, take the
+// balanced cut instead, at the largest k <= kDecodeBalancedRounds rounds of
+// resident workgroups whose chunk count fits that many rounds, and launch its
+// chunks longest first (measured on the 64-head 64k GQA rings at batch 12 to
+// 48: 2 to 6 % faster than the cuts above; at batch 4 and 8, where those
+// cuts fit one round, it was slower, hence the condition).
+constexpr int64_t kDecodeBalancedRounds = 2;
 // Decode workgroups resident per CU (256 threads each, one wave per SIMD):
 // the occupancy the compiled kernels reach, set by their register and LDS use.
 constexpr int kDecodeResidentD64 = 5;
@@ -76,13 +91,19 @@ inline int decode_resident(int D) {
   return kCUs * (D == 128 ? kDecodeResidentD128 : kDecodeResidentD64);
 }
 // Chunk length of a ring of s slots under cut c (every chunk but the last).
-inline int32_t cut_step(int32_t s, DecodeCut c) {
-  if (!c.even || s <= 0) return c.size;
-  const int32_t n = (s + c.size - 1) / c.size;
-  const int32_t len = (s + n - 1) / n;
-  return (len + 31) / 32 * 32;
+inline int32_t cut_step(int32_t s, const DecodeCut& c) {
+  if (c.kind == CutKind::kFixed || s <= 0) return c.size;
+  int64_t n;
+  if (c.kind == CutKind::kEven) {
+    n = (s + c.size - 1) / c.size;
+  } else {
+    n = ((int64_t)s * c.k + c.total / 2) / c.total;
+    if (n < 1) n = 1;
+  }
+  const int64_t len = (s + n - 1) / n;
+  return (int32_t)((len + 31) / 32 * 32);
 }
-inline int32_t cut_count(int32_t s, DecodeCut c) {
+inline int32_t cut_count(int32_t s, const DecodeCut& c) {
   if (s <= 0) return 0;
   const int32_t step = cut_step(s, c);
   return (s + step - 1) / step;
@@ -100,6 +121,7 @@ struct PlanDevice {
   int4* prefill_items = nullptr;    // launch table {b*Hq + h_q, q_tile, kt_lo, kt_hi}, bq < 0: padding
   int4* decode_chunks = nullptr;    // [n_chunks] {b*Hkv + h, first_slot, n_slots, chunks_of_ring}
   int2* head_chunks = nullptr;      // [B*Hkv] {first chunk index, chunk count}
+  int32_t* decode_order = nullptr;  // [n_chunks] chunk of each decode workgroup; null: the identity
 };
 
 }  // namespace moa
@@ -129,8 +151,9 @@ struct moa_plan {
   int64_t n_prefill_units = 0;            // units of all sequences
   std::vector<int32_t> decode_chunks;     // 4 per chunk, all sequences: {b*Hkv + h, first, n, chunks_of_ring}
   std::vector<int32_t> head_chunks;       // 2 per (b, h): {first chunk, count}
-  int32_t decode_chunk = moa::kDecodeChunk;   // longest chunk the cut allows
-  bool decode_even = false;               // even cut (else fixed)
+  std::vector<int32_t> decode_order;      // launch order of the chunks (balanced cut), else empty
+  moa::DecodeCut decode_cut{moa::CutKind::kFixed, moa::kDecodeChunk};
+  int32_t decode_chunk = moa::kDecodeChunk;   // longest chunk of the cut
   int64_t n_chunks = 0;                   // decode chunks of all sequences
   bool any_split = false;                 // some ring has more than one chunk
   moa::PlanDevice dev;

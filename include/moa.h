@@ -205,22 +205,31 @@ int64_t moa_max_batch(const moa_problem* problem, uint64_t budget_bytes);
  * entries, padding included, a multiple of 8) and runs that table once per
  * sequence: sequence b's unit at entry e runs in workgroup b*T + e.
  * Decode chunks are int32 quadruples {b, h_kv, first_slot, n_slots} of all
- * sequences, in launch order (rings in (b, h_kv) order, each ring's chunks
- * from its first slot); every chunk starts at a multiple of 32 slots and
- * holds at most moa_plan_decode_chunk() = c slots.  The fixed cut takes c =
- * 1024 when G = 1, else the largest of 3072, 2048, 1536 that still gives the
- * plan at least 2048 chunks (1024 if none does), and cuts each ring into
- * chunks of c slots, the last one shorter.  A plan whose fixed cut has fewer
- * than 8 * R chunks (R = resident decode workgroups: 512 for D = 128, 1280
- * for D = 64) may take an even cut instead: a ring of s slots gets
- * ceil(s / c) chunks of ceil(s / ceil(s / c)) slots rounded up to a multiple
- * of 32, the last one shorter.  The planner models a launch as chunks taken
- * in order, each by the first of R slots to free, which it holds for n_slots
- * + 32; of the even cuts at c in {1024, 1536, 2048, 2560, 3072, 3584, 4096,
- * 4608, 5120, 6144, 8192}, c no smaller than the fixed cut's, it takes the
- * one whose modeled end is earliest (the smaller c on a tie) if that end is
- * at most 92% of the fixed cut's, else the fixed cut.  An even cut never has
- * more chunks than the fixed cut.  Pass out = NULL to get the count; the
+ * sequences, in launch order; every chunk starts at a multiple of 32 slots and
+ * holds at most moa_plan_decode_chunk() slots.  Let R be the decode
+ * workgroups resident at once (512 for D = 128, 1280 for D = 64).  The fixed
+ * cut takes c = 1024 when G = 1, else the largest of 3072, 2048, 1536 that
+ * still gives the plan at least 2048 chunks (1024 if none does), and cuts
+ * each ring into chunks of c slots, the last one shorter.  A plan whose fixed
+ * cut has fewer than 8 * R chunks may take an even cut instead: a ring of s
+ * slots gets ceil(s / c) chunks of ceil(s / ceil(s / c)) slots rounded up to
+ * a multiple of 32, the last one shorter.  The planner models a launch as
+ * chunks taken in order, each by the first of R slots to free, which it holds
+ * for n_slots + 32; of the even cuts at c in {1024, 1536, 2048, 2560, 3072,
+ * 3584, 4096, 4608, 5120, 6144, 8192}, c no smaller than the fixed cut's, it
+ * takes the one whose modeled end is earliest (the smaller c on a tie) if
+ * that end is at most 92% of the fixed cut's, else the fixed cut.  Then, when
+ * G > 1, the cut so far has more than R chunks and the plan has at most R
+ * rings, it takes the balanced cut: with total the slots of all rings, a
+ * ring of s slots gets n = max(1, floor((s * k + floor(total / 2)) / total))
+ * chunks of ceil(s / n) slots rounded up to a multiple of 32, the last one
+ * shorter, for the largest k <= 2 * R whose chunk count is at most 2 * R.  A
+ * fixed or even cut launches rings in (b, h_kv) order, each ring's chunks
+ * from its first slot, and moa_plan_decode_chunk() is c; a balanced cut
+ * launches the same chunks longest first (a stable sort of that order) and
+ * reports its longest chunk.  The even and balanced cuts never have more
+ * chunks than the fixed cut or 2 * R, whichever is larger.  Pass out = NULL
+ * to get the count; the
  * return value is the item count (>= 0) or a negative moa_status. */
 int64_t moa_plan_prefill_items(moa_plan_t plan, int32_t* out);
 int64_t moa_plan_decode_chunks(moa_plan_t plan, int32_t* out);

@@ -143,10 +143,11 @@ def test_decode_argument_errors(moa):
         plan.decode(q[:, :1], kc, vc, 64, o, plan.new_workspace())
 
 
-# Grouped heads at a size where the plan takes 3072-slot chunks (the rule of
-# moa_plan_decode_chunk): B64 Hq64 Hkv8 D128 N24576 with the 64-head 64k rules.
-GQA_3072 = workloads.Workload("gqa_chunk3072", "decode", 64, 64, 8, 128, 24576, "bf16", 3, "c4",
-                              2005, "B64 Hq64 Hkv8 D128 N24576 bf16, 3072-slot decode chunks")
+# Grouped heads at a size where the plan takes the fixed cut at 3072 slots (the rule of
+# moa_plan_decode_chunks: more rings than one round of resident workgroups, and at least
+# eight rounds of chunks): B128 Hq64 Hkv8 D128 N24576 with the 64-head 64k rules.
+GQA_3072 = workloads.Workload("gqa_chunk3072", "decode", 128, 64, 8, 128, 24576, "bf16", 3, "c4",
+                              2005, "B128 Hq64 Hkv8 D128 N24576 bf16, 3072-slot decode chunks")
 
 
 @pytest.mark.parametrize("name", ["c2_decode", "c3_decode", "c4_decode", "gqa_chunk3072"])
@@ -159,13 +160,14 @@ def test_decode_full_size_every_head(moa, name):
     lay = Layout(alpha, beta, w.batch, w.head_dim, w.n_prompt)
     assert plan.cache_elems == lay.total_slots * w.head_dim
     ch = plan.decode_chunks()
-    even = bool(np.any((ch[:, 3] != plan.decode_chunk) & (ch[:, 2] + ch[:, 3] < lay.spans[ch[:, 1]])))
-    log(f"{name}: decode chunk {plan.decode_chunk} slots ({'even' if even else 'fixed'} cut), "
-        f"{len(ch)} chunks")
-    if name == "gqa_chunk3072":
-        assert plan.decode_chunk == 3072 and not even
-    if name == "c4_decode":             # the even cut at full size (4448..4608-slot chunks)
-        assert plan.decode_chunk == 4608 and even
+    uneven = bool(np.any((ch[:, 3] != plan.decode_chunk) & (ch[:, 2] + ch[:, 3] < lay.spans[ch[:, 1]])))
+    ring_order = bool((np.diff(ch[:, 0] * w.n_kv_heads + ch[:, 1]) >= 0).all())
+    log(f"{name}: decode chunk {plan.decode_chunk} slots, {len(ch)} chunks"
+        f"{', launched longest first' if not ring_order else ''}")
+    if name == "gqa_chunk3072":         # the fixed cut
+        assert plan.decode_chunk == 3072 and not uneven and ring_order
+    if name == "c4_decode":             # the balanced cut, launched longest first
+        assert not ring_order and (np.diff(ch[:, 3]) <= 0).all() and len(ch) <= 1024
     log(f"{name}: filling {2 * plan.cache_elems * 2 / 1e9:.2f} GB of rings")
     kc = workloads.device_normal_(torch.empty(plan.cache_elems, dtype=torch.bfloat16,
                                               device="cuda"), 81)

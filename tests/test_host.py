@@ -234,27 +234,34 @@ def test_prefill_items_full_size_tables(moa):
         plan.close()
 
 
-def _cut_step(s, c, even):
-    """Chunk length of a ring of s slots: c for the fixed cut; for the even cut, the ring's
-    ceil(s / c) chunks share ceil(s / count) slots rounded up to a multiple of 32."""
-    if not even:
-        return c
-    n = -(-s // c)
+def _cut_step(s, cut):
+    """Chunk length of a ring of s slots under a cut: ("fixed", c) -> c; ("even", t) -> the
+    ring's ceil(s / t) chunks share ceil(s / count) slots, rounded up to a multiple of 32;
+    ("balanced", k, total) -> the same with max(1, floor((s k + floor(total / 2)) / total))
+    chunks."""
+    if cut[0] == "fixed":
+        return cut[1]
+    if cut[0] == "even":
+        n = -(-s // cut[1])
+    else:
+        _, k, total = cut
+        n = max(1, (s * k + total // 2) // total)
     return -(-(-(-s // n)) // 32) * 32
 
 
 def _decode_cut(spans, g, d):
-    """The decode cut include/moa.h states, restated: (chunk size, even) for a plan whose rings
-    have these spans in launch order, g query heads per KV head, head dimension d."""
-    def count(c, even):
-        return sum(-(-int(s) // _cut_step(int(s), c, even)) for s in spans)
+    """The decode cut include/moa.h states, restated, for a plan whose rings have these spans
+    in (b, h) order, g query heads per KV head, head dimension d."""
+    spans = [int(x) for x in spans]
 
-    def makespan(c, even, slots):
+    def count(cut):
+        return sum(-(-s // _cut_step(s, cut)) for s in spans)
+
+    def makespan(cut, slots):
         free = [0] * slots           # when each resident workgroup slot frees
         end = 0
         for s in spans:
-            s = int(s)
-            st = _cut_step(s, c, even)
+            st = _cut_step(s, cut)
             for first in range(0, s, st):
                 t = heapq.heappop(free) + min(st, s - first) + 32
                 heapq.heappush(free, t)
@@ -263,48 +270,60 @@ def _decode_cut(spans, g, d):
 
     c = 1024
     if g > 1:
-        c = next((x for x in (3072, 2048, 1536) if count(x, False) >= 2048), 1024)
+        c = next((x for x in (3072, 2048, 1536) if count(("fixed", x)) >= 2048), 1024)
     slots = 256 * (2 if d == 128 else 5)
-    if count(c, False) >= 8 * slots:
-        return c, False
-    t_fixed = makespan(c, False, slots)
-    best = min((makespan(t, True, slots), t) for t in
-               (1024, 1536, 2048, 2560, 3072, 3584, 4096, 4608, 5120, 6144, 8192) if t >= c)
-    return (best[1], True) if best[0] * 100 <= t_fixed * 92 else (c, False)
+    cut = ("fixed", c)
+    if count(cut) < 8 * slots:
+        t_fixed = makespan(cut, slots)
+        best = min((makespan(("even", t), slots), t) for t in
+                   (1024, 1536, 2048, 2560, 3072, 3584, 4096, 4608, 5120, 6144, 8192) if t >= c)
+        if best[0] * 100 <= t_fixed * 92:
+            cut = ("even", best[1])
+    if g > 1 and count(cut) > slots and len(spans) <= slots:
+        total = sum(spans)
+        for k in range(2 * slots, len(spans) - 1, -1):
+            if count(("balanced", k, total)) <= 2 * slots:
+                return ("balanced", k, total)
+    return cut
 
 
-def _cut_table(spans, hkv, c, even):
-    """{b, h, first, n} of every chunk, rings in (b, h) order."""
+def _cut_table(spans, hkv, cut):
+    """{b, h, first, n} of every chunk in launch order: rings in (b, h) order, each ring's
+    chunks from its first slot; a balanced cut launches them longest first (stable)."""
     rows = []
     for i, s in enumerate(int(x) for x in spans):
-        st = _cut_step(s, c, even)
+        st = _cut_step(s, cut)
         rows += [(i // hkv, i % hkv, f, min(st, s - f)) for f in range(0, s, st)]
+    if cut[0] == "balanced":
+        rows = sorted(rows, key=lambda r: -r[3])
     return np.array(rows, dtype=np.int32).reshape(-1, 4)
 
 
-@pytest.mark.parametrize("batch,hq,hkv,d,n,cut", [
-    (64, 32, 32, 128, 16384, (1024, False)), (16, 64, 8, 128, 65536, (4608, True)),
-    (8, 64, 8, 128, 65536, (4608, True)), (4, 64, 8, 128, 65536, (2560, True)),
-    (32, 64, 8, 128, 65536, (3072, False)), (64, 256, 32, 128, 16384, None),
-    (1, 8, 2, 128, 1000, None), (2000, 8, 1, 128, 4096, (3072, True)),
-    (3, 8, 2, 64, 20000, None), (40, 16, 2, 64, 30000, None), (2, 40, 40, 128, 32768, None)])
-def test_decode_chunk_rule(moa, batch, hq, hkv, d, n, cut):
-    """The fixed cut (1024 slots for ungrouped heads; with G > 1 the largest of 3072, 2048, 1536
-    that leaves at least 2048 chunks, else 1024), replaced by an even cut where the dispatch
-    model include/moa.h states finishes at least 8% sooner; the chunk table is rebuilt from
-    the rule.  `cut` pins the outcome where it is known (the 64-head 64k rules at batch 4 to
-    32, the 32-head 16k rules at batch 64)."""
+@pytest.mark.parametrize("batch,hq,hkv,d,n,kind", [
+    (64, 32, 32, 128, 16384, "fixed"), (16, 64, 8, 128, 65536, "balanced"),
+    (8, 64, 8, 128, 65536, "even"), (4, 64, 8, 128, 65536, "even"),
+    (32, 64, 8, 128, 65536, "balanced"), (72, 64, 8, 128, 65536, "fixed"),
+    (128, 64, 8, 128, 24576, "fixed"), (64, 256, 32, 128, 16384, None),
+    (1, 8, 2, 128, 1000, None), (2000, 8, 1, 128, 4096, "even"),
+    (3, 8, 2, 64, 20000, None), (40, 16, 2, 64, 30000, None), (2, 40, 40, 128, 32768, None),
+    (6, 32, 4, 64, 60000, None)])
+def test_decode_chunk_rule(moa, batch, hq, hkv, d, n, kind):
+    """The fixed cut (1024 slots for ungrouped heads; with G > 1 the largest of 3072, 2048,
+    1536 that leaves at least 2048 chunks, else 1024); an even cut where the dispatch model
+    include/moa.h states finishes at least 8 % sooner; for grouped heads that still need more
+    than one round of resident workgroups, the balanced cut launched longest first.  The
+    chunk table is rebuilt from the rule.  `kind` pins the outcome where it is known."""
     alpha, beta = workloads.rules("c4_decode")
     alpha, beta = (list(alpha) * 8)[:hkv], (list(beta) * 8)[:hkv]
     plan = moa.Plan(batch, hq, hkv, d, n, alpha, beta, host_only=True)
     s = np.tile(oracle.spans(alpha, beta, n), batch)
-    c, even = _decode_cut(s, hq // hkv, d)
-    if cut is not None:
-        assert (c, even) == cut
-    assert plan.decode_chunk == c
+    cut = _decode_cut(s, hq // hkv, d)
+    if kind is not None:
+        assert cut[0] == kind, cut
     ch = plan.decode_chunks()
-    assert len(ch) == int(np.sum((s + c - 1) // c))
-    assert np.array_equal(ch, _cut_table(s, hkv, c, even))
+    want = _cut_table(s, hkv, cut)
+    assert np.array_equal(ch, want)
+    assert plan.decode_chunk == (int(want[:, 3].max()) if cut[0] == "balanced" else cut[1])
     _check_chunks(plan, ch)
     plan.close()
 
@@ -324,14 +343,15 @@ def test_decode_chunks_cover_rings(moa, name):
 
 def _check_chunks(plan, ch):
     """Every slot of every ring (b, h) in exactly one chunk of at most decode_chunk slots,
-    chunks in (b, h) order."""
+    starting on a 32-slot block; the launch order either keeps rings in (b, h) order or runs
+    the chunks longest first."""
     c = plan.decode_chunk
-    assert (np.diff(ch[:, 0] * plan.n_kv_heads + ch[:, 1]) >= 0).all()
+    ring_order = bool((np.diff(ch[:, 0] * plan.n_kv_heads + ch[:, 1]) >= 0).all())
+    assert ring_order or bool((np.diff(ch[:, 3]) <= 0).all())
     for b in range(plan.batch):
         for h in range(plan.n_kv_heads):
             s = int(plan.seq_spans[b, h])
             mine = ch[(ch[:, 0] == b) & (ch[:, 1] == h)]
-            assert len(mine) == -(-s // c)
             covered = np.zeros(s, dtype=int)
             for _, _, first, cnt in mine:
                 assert 1 <= cnt <= c and first % 32 == 0
