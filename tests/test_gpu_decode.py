@@ -150,12 +150,22 @@ GQA_3072 = workloads.Workload("gqa_chunk3072", "decode", 128, 64, 8, 128, 24576,
                               2005, "B128 Hq64 Hkv8 D128 N24576 bf16, 3072-slot decode chunks")
 
 
-@pytest.mark.parametrize("name", ["c2_decode", "c3_decode", "c4_decode", "gqa_chunk3072"])
+# Grouped heads of group size 4 and 2 at sizes where the plan takes the balanced cut,
+# launched longest first (the rule of moa_plan_decode_chunks), with the 64-head 64k rules.
+GQA_BAL4 = workloads.Workload("gqa_balanced_g4", "decode", 16, 32, 8, 128, 24576, "bf16", 3, "c4",
+                              2006, "B16 Hq32 Hkv8 D128 N24576 bf16, balanced decode cut")
+GQA_BAL2 = workloads.Workload("gqa_balanced_g2", "decode", 32, 16, 8, 128, 12288, "bf16", 3, "c4",
+                              2007, "B32 Hq16 Hkv8 D128 N12288 bf16, balanced decode cut")
+EXTRA = {w.name: w for w in (GQA_3072, GQA_BAL4, GQA_BAL2)}
+
+
+@pytest.mark.parametrize("name", ["c2_decode", "c3_decode", "c4_decode", "gqa_chunk3072",
+                                  "gqa_balanced_g4", "gqa_balanced_g2"])
 def test_decode_full_size_every_head(moa, name):
     """Full-size rings (device-filled with seeded N(0,1)), three steps, every (b, h) of every
     step checked against the oracle's explicit-window decode."""
-    w = GQA_3072 if name == "gqa_chunk3072" else workloads.WORKLOADS[name]
-    alpha, beta = workloads.rules("c4_decode" if name == "gqa_chunk3072" else name)
+    w = EXTRA.get(name) or workloads.WORKLOADS[name]
+    alpha, beta = workloads.rules("c4_decode" if name in EXTRA else name)
     plan = moa.Plan(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, alpha, beta)
     lay = Layout(alpha, beta, w.batch, w.head_dim, w.n_prompt)
     assert plan.cache_elems == lay.total_slots * w.head_dim
@@ -166,7 +176,7 @@ def test_decode_full_size_every_head(moa, name):
         f"{', launched longest first' if not ring_order else ''}")
     if name == "gqa_chunk3072":         # the fixed cut
         assert plan.decode_chunk == 3072 and not uneven and ring_order
-    if name == "c4_decode":             # the balanced cut, launched longest first
+    if name in ("c4_decode", "gqa_balanced_g4", "gqa_balanced_g2"):   # balanced, longest first
         assert not ring_order and (np.diff(ch[:, 3]) <= 0).all() and len(ch) <= 1024
     log(f"{name}: filling {2 * plan.cache_elems * 2 / 1e9:.2f} GB of rings")
     kc = workloads.device_normal_(torch.empty(plan.cache_elems, dtype=torch.bfloat16,
