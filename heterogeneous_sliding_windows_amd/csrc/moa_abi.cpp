@@ -84,7 +84,7 @@ DecodeCut decode_cut(const std::vector<int32_t>& span, int64_t copies, int G, in
     }
   }
   uint64_t rings;
-  if (G > 1 && *n_chunks > slots && !__builtin_mul_overflow((uint64_t)copies, (uint64_t)span.size(), &rings) &&
+  if (G >= kDecodeBalancedMinG && *n_chunks > slots && !__builtin_mul_overflow((uint64_t)copies, (uint64_t)span.size(), &rings) &&
       rings <= (uint64_t)slots) {
     int64_t total = 0;
     for (const int32_t s : span) total += s;

@@ -74,14 +74,17 @@ constexpr int kDecodeEvenTargets[11] = {1024, 1536, 2048, 2560, 3072, 3584,
 constexpr int64_t kDecodeModelRounds = 8;
 constexpr int64_t kDecodeModelOverhead = 32;
 constexpr int64_t kDecodeModelGainPct = 92;
-// Grouped heads (G > 1) whose cut so far still takes more than one round of
-// resident workgroups, in plans of at most one round of rings, take the
-// balanced cut instead, at the largest k <= kDecodeBalancedRounds rounds of
-// resident workgroups whose chunk count fits that many rounds, and launch its
-// chunks longest first (measured on the 64-head 64k GQA rings at batch 12 to
-// 48: 2 to 6 % faster than the cuts above; at batch 4 and 8, where those
-// cuts fit one round, it was slower, hence the condition).
+// Groups of at least kDecodeBalancedMinG query heads whose cut so far still
+// takes more than one round of resident workgroups, in plans of at most one
+// round of rings, take the balanced cut instead, at the largest k <=
+// kDecodeBalancedRounds rounds of resident workgroups whose chunk count fits
+// that many rounds, and launch its chunks longest first.  Measured on the
+// 64-head 64k GQA rings (G = 8) at batch 12 to 64: 2 to 6 % faster than the
+// cuts above; at batch 4 and 8, where those cuts fit one round, it was
+// slower, hence the round condition.  Groups of 4 gained up to 3 %; groups of
+// 2, whose chunks publish few partial rows, moved by -1.6 to +2.2 %.
 constexpr int64_t kDecodeBalancedRounds = 2;
+constexpr int kDecodeBalancedMinG = 4;
 // Decode workgroups resident per CU (256 threads each, one wave per SIMD):
 // the occupancy the compiled kernels reach, set by their register and LDS use.
 constexpr int kDecodeResidentD64 = 5;

@@ -219,7 +219,7 @@ int64_t moa_max_batch(const moa_problem* problem, uint64_t budget_bytes);
  * 3584, 4096, 4608, 5120, 6144, 8192}, c no smaller than the fixed cut's, it
  * takes the one whose modeled end is earliest (the smaller c on a tie) if
  * that end is at most 92% of the fixed cut's, else the fixed cut.  Then, when
- * G > 1, the cut so far has more than R chunks and the plan has at most R
+ * G >= 4, the cut so far has more than R chunks and the plan has at most R
  * rings, it takes the balanced cut: with total the slots of all rings, a
  * ring of s slots gets n = max(1, floor((s * k + floor(total / 2)) / total))
  * chunks of ceil(s / n) slots rounded up to a multiple of 32, the last one

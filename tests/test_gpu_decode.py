@@ -150,17 +150,18 @@ GQA_3072 = workloads.Workload("gqa_chunk3072", "decode", 128, 64, 8, 128, 24576,
                               2005, "B128 Hq64 Hkv8 D128 N24576 bf16, 3072-slot decode chunks")
 
 
-# Grouped heads of group size 4 and 2 at sizes where the plan takes the balanced cut,
-# launched longest first (the rule of moa_plan_decode_chunks), with the 64-head 64k rules.
+# Grouped heads at sizes where the plan takes the balanced cut, launched longest first (the
+# rule of moa_plan_decode_chunks), with the 64-head 64k rules: group size 4 at head dim 128,
+# and group size 8 at head dim 64 (two rounds of 1280 resident workgroups).
 GQA_BAL4 = workloads.Workload("gqa_balanced_g4", "decode", 16, 32, 8, 128, 24576, "bf16", 3, "c4",
                               2006, "B16 Hq32 Hkv8 D128 N24576 bf16, balanced decode cut")
-GQA_BAL2 = workloads.Workload("gqa_balanced_g2", "decode", 32, 16, 8, 128, 12288, "bf16", 3, "c4",
-                              2007, "B32 Hq16 Hkv8 D128 N12288 bf16, balanced decode cut")
-EXTRA = {w.name: w for w in (GQA_3072, GQA_BAL4, GQA_BAL2)}
+GQA_BAL_D64 = workloads.Workload("gqa_balanced_d64", "decode", 32, 64, 8, 64, 32768, "bf16", 3,
+                                 "c4", 2007, "B32 Hq64 Hkv8 D64 N32768 bf16, balanced decode cut")
+EXTRA = {w.name: w for w in (GQA_3072, GQA_BAL4, GQA_BAL_D64)}
 
 
 @pytest.mark.parametrize("name", ["c2_decode", "c3_decode", "c4_decode", "gqa_chunk3072",
-                                  "gqa_balanced_g4", "gqa_balanced_g2"])
+                                  "gqa_balanced_g4", "gqa_balanced_d64"])
 def test_decode_full_size_every_head(moa, name):
     """Full-size rings (device-filled with seeded N(0,1)), three steps, every (b, h) of every
     step checked against the oracle's explicit-window decode."""
@@ -176,8 +177,9 @@ def test_decode_full_size_every_head(moa, name):
         f"{', launched longest first' if not ring_order else ''}")
     if name == "gqa_chunk3072":         # the fixed cut
         assert plan.decode_chunk == 3072 and not uneven and ring_order
-    if name in ("c4_decode", "gqa_balanced_g4", "gqa_balanced_g2"):   # balanced, longest first
-        assert not ring_order and (np.diff(ch[:, 3]) <= 0).all() and len(ch) <= 1024
+    if name in ("c4_decode", "gqa_balanced_g4", "gqa_balanced_d64"):   # balanced, longest first
+        assert not ring_order and (np.diff(ch[:, 3]) <= 0).all()
+        assert len(ch) <= 2 * 256 * (2 if w.head_dim == 128 else 5)
     log(f"{name}: filling {2 * plan.cache_elems * 2 / 1e9:.2f} GB of rings")
     kc = workloads.device_normal_(torch.empty(plan.cache_elems, dtype=torch.bfloat16,
                                               device="cuda"), 81)

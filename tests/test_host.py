@@ -279,7 +279,7 @@ def _decode_cut(spans, g, d):
                    (1024, 1536, 2048, 2560, 3072, 3584, 4096, 4608, 5120, 6144, 8192) if t >= c)
         if best[0] * 100 <= t_fixed * 92:
             cut = ("even", best[1])
-    if g > 1 and count(cut) > slots and len(spans) <= slots:
+    if g >= 4 and count(cut) > slots and len(spans) <= slots:
         total = sum(spans)
         for k in range(2 * slots, len(spans) - 1, -1):
             if count(("balanced", k, total)) <= 2 * slots:
@@ -310,8 +310,8 @@ def _cut_table(spans, hkv, cut):
 def test_decode_chunk_rule(moa, batch, hq, hkv, d, n, kind):
     """The fixed cut (1024 slots for ungrouped heads; with G > 1 the largest of 3072, 2048,
     1536 that leaves at least 2048 chunks, else 1024); an even cut where the dispatch model
-    include/moa.h states finishes at least 8 % sooner; for grouped heads that still need more
-    than one round of resident workgroups, the balanced cut launched longest first.  The
+    include/moa.h states finishes at least 8 % sooner; for groups of 4 or more heads that still
+    need more than one round of resident workgroups, the balanced cut launched longest first.  The
     chunk table is rebuilt from the rule.  `kind` pins the outcome where it is known."""
     alpha, beta = workloads.rules("c4_decode")
     alpha, beta = (list(alpha) * 8)[:hkv], (list(beta) * 8)[:hkv]
