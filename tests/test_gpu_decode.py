@@ -229,3 +229,81 @@ def test_decode_full_size_every_head(moa, name):
     bad = [(b, h, t, e) for (b, h), (e, t) in zip(pairs, errs) if e > TOL]
     assert not bad, (name, bad[:8])
     log(f"{name}: every (b, h) of {t_steps} steps, worst err {worst:.3e}")
+
+
+@pytest.mark.parametrize("name", ["c2_decode", "c3_decode", "c4_decode"])
+def test_decode_full_size_long_run(moa, name):
+    """All T steps of a decode workload through the fused call (the bench's step) on
+    full-size rings: every (b, h) checked against the oracle at steps 0, 1, 2, T/2 and T-1,
+    the first and last sequence at every step, and their rings bit for bit after the last
+    step (by then the steps have overwritten the oldest T slots of every ring)."""
+    w = workloads.WORKLOADS[name]
+    alpha, beta = workloads.rules(name)
+    plan = moa.Plan(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_prompt, alpha, beta)
+    lay = Layout(alpha, beta, w.batch, w.head_dim, w.n_prompt)
+    t_steps, n, g, bsz = w.steps, w.n_prompt, w.n_q_heads // w.n_kv_heads, w.batch
+    log(f"{name} long run: {t_steps} fused steps, filling {2 * plan.cache_elems * 2 / 1e9:.2f} GB")
+    kc = workloads.device_normal_(torch.empty(plan.cache_elems, dtype=torch.bfloat16,
+                                              device="cuda"), 83)
+    vc = workloads.device_normal_(torch.empty(plan.cache_elems, dtype=torch.bfloat16,
+                                              device="cuda"), 84)
+    kc_h, vc_h = kc.cpu(), vc.cpu()       # the prompt rings, for the oracle's history
+    ws = plan.new_workspace()
+    qs, ks, vs = workloads.decode_step_inputs(bsz, w.n_q_heads, w.n_kv_heads, t_steps,
+                                              w.head_dim, "bf16", w.data_seed + 7)
+    all_b = {0, 1, 2, t_steps // 2, t_steps - 1}
+    edge_b = sorted({0, bsz - 1})
+    outs = {}
+    o = torch.empty(bsz, w.n_q_heads, w.head_dim, dtype=torch.bfloat16, device="cuda")
+    for t in range(t_steps):
+        plan.append_decode(qs[t].cuda(), kc, vc, ks[t].cuda(), vs[t].cuda(), n + t, o, ws)
+        outs[t] = f64(o) if t in all_b else f64(o[edge_b])
+        if t % 64 == 0:
+            log(f"{name}: step {t}")
+    torch.cuda.synchronize()
+    ks64, vs64, qs64 = f64(ks), f64(vs), f64(qs)
+
+    def check(pair):
+        b, h = pair
+        s = int(lay.spans[h])
+        order = np.argsort(ring_positions(s, n - 1))   # the prompt tail, by position
+        hist_k = np.concatenate([f64(ring_k(kc_h, lay, b, h))[order], ks64[:, b, h]])
+        hist_v = np.concatenate([f64(ring_v(vc_h, lay, b, h))[order], vs64[:, b, h]])
+        steps = range(t_steps) if b in edge_b else sorted(all_b)
+        res = (0.0, -1)
+        for t in steps:
+            got = outs[t][b] if t in all_b else outs[t][edge_b.index(b)]
+            want = oracle.decode_step(qs64[t, b, h * g:(h + 1) * g], hist_k[:s + t + 1],
+                                      hist_v[:s + t + 1], np.arange(n - s, n + t + 1), n + t, s)
+            res = max(res, (max_err(got[h * g:(h + 1) * g], want), t))
+        return res
+
+    pairs = [(b, h) for b in range(bsz) for h in range(w.n_kv_heads)]
+    with threadpool_limits(1), ThreadPoolExecutor(8) as ex:
+        errs = []
+        for i in range(0, len(pairs), 256):
+            errs += list(ex.map(check, pairs[i:i + 256]))
+            log(f"{name}: checked {min(i + 256, len(pairs))} of {len(pairs)} (b, h)")
+    worst = max(e for e, _ in errs)
+    bad = [(b, h, t, e) for (b, h), (e, t) in zip(pairs, errs) if e > TOL]
+    assert not bad, (name, bad[:8])
+    log(f"{name}: {t_steps} steps, worst err {worst:.3e}")
+
+    # rings of the first and last sequence after the last step, bit for bit
+    kc_e, vc_e = kc.cpu(), vc.cpu()
+    p_last = n - 1 + t_steps
+    for b in edge_b:
+        for h in range(w.n_kv_heads):
+            s = int(lay.spans[h])
+            order = np.argsort(ring_positions(s, n - 1))
+            hk = torch.cat([ring_k(kc_h, lay, b, h)[order], ks[:, b, h]])
+            hv = torch.cat([ring_v(vc_h, lay, b, h)[order], vs[:, b, h]])
+            pos = np.arange(n - s, n + t_steps)
+            exp_k, held = oracle.ring_expected(hk.view(torch.int16).numpy(), pos, s, p_last)
+            exp_v, _ = oracle.ring_expected(hv.contiguous().view(torch.int16).numpy(), pos, s,
+                                            p_last)
+            assert (held == ring_positions(s, p_last)).all()
+            assert np.array_equal(ring_k(kc_e, lay, b, h).view(torch.int16).numpy(), exp_k), (b, h)
+            assert np.array_equal(ring_v(vc_e, lay, b, h).contiguous().view(torch.int16).numpy(),
+                                  exp_v), (b, h)
+    log(f"{name}: rings of sequences {edge_b} match the oracle after {t_steps} steps")
