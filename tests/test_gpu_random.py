@@ -16,6 +16,8 @@ bf16 cases also run three decode steps (fused, separate, fused) and check their 
 and the rings again. Spans and ring locations come from the oracle alone.
 """
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -28,7 +30,7 @@ pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
 _BITS = {torch.bfloat16: torch.int16, torch.float32: torch.int32}
-N_CASES = 24
+N_CASES = int(os.environ.get("MOA_RANDOM_CASES", "24"))   # more for an extended run
 
 
 def _bits(t):
