@@ -19,30 +19,32 @@
 // by Npad - N_b rows and work in its own positions 0 .. N_b - 1; padding rows
 // are neither read nor written.
 //
-// bf16 kernel (4 waves, 32 query rows each):
+// bf16 kernel (4 waves, 32 query rows each; three workgroups a CU):
 //  * S^T = K Q^T on 32x32x16 bf16 MFMA, so each lane owns one query row and
 //    the row max needs one exchange with the partner lane (l ^ 32);
 //  * key rows of a 32-key MFMA tile are permuted (row m = 16a + 8b + 4h + c
 //    reads key 16a + 8h + 4b + c), which puts the scores of lane half h on
 //    keys 16j + 8h .. +7 of P.V step j: the P^T operand is the lane's own
 //    scores, converted to bf16, with no data movement;
-//  * K and V tiles go from memory straight into LDS (16-byte LDS-direct
-//    buffer loads, no staging registers), in a chunk-swizzled layout that
-//    both fragment reads meet without bank conflicts; the V^T operand of the
-//    P.V product (8 consecutive keys of one dimension per lane) comes from
-//    two transposed LDS reads (ds_read_b64_tr_b16);
-//  * LDS tiles are double-buffered: tile t+1's loads are issued before tile
-//    t is computed (one wait and one barrier a tile);
+//  * each 64-key tile of the unit is streamed as two 32-key sub-tiles, which
+//    go from memory straight into LDS (16-byte LDS-direct buffer loads, no
+//    staging registers), in a chunk-swizzled layout that both fragment reads
+//    meet without bank conflicts; the V^T operand of the P.V product (8
+//    consecutive keys of one dimension per lane) comes from two transposed
+//    LDS reads (ds_read_b64_tr_b16).  32 KB of LDS and 166 VGPRs a lane let
+//    three workgroups share a CU;
+//  * LDS sub-tiles are double-buffered: sub-tile t+1's loads are issued
+//    before sub-tile t is computed (one wait and one barrier a sub-tile);
 //  * O goes through LDS: each wave writes its normalised rows to LDS and
 //    stores them as whole 16-byte chunks, four complete rows per store
 //    instruction;
-//  * masks are evaluated only on tiles a wave's rows do not fully keep, and a
-//    wave skips tiles none of its rows keep;
+//  * masks are evaluated only on sub-tiles a wave's rows do not fully keep,
+//    and a wave skips sub-tiles none of its rows keep;
 //  * online softmax in fp32 with exp2: the scores leave the matrix cores raw
 //    (fp32) and 1/sqrt(D)*log2(e) is applied in fp32 before each
 //    exponential; O and the row sum are rescaled only when a row's max grows
-//    by more than 8 in the exp2 domain (a factor of 2^8), which most tiles
-//    after the first never trigger.
+//    by more than 8 in the exp2 domain (a factor of 2^8), which most
+//    sub-tiles after the first never trigger.
 //
 // f32 kernel (the float32 dtype): the same units and softmax on fp32 matrix
 // cores (v_mfma_f32_16x16x4f32), K/V tiles in LDS, an exact running max (no
@@ -50,13 +52,13 @@
 //
 // Fused handoff (RING = true): besides o, the launch writes positions
 // N - S_h .. N - 1 of every (b, h_kv) into the KV rings, as an append of the
-// whole prompt would.  Key tile kt is the diagonal tile of query tile
-// kt*BN/BM, whose item always streams it; the workgroup of the first query
-// head of each KV group (g = 0) stores the rows of its diagonal tiles that the
-// ring keeps, reading them from LDS.  Every ring row is therefore written
-// once, and K/V are read from HBM once.  The diagonal tiles are the unit's
-// last one or two, still in their buffers when the loop ends, so the stores
-// follow the loop and the loop itself is the plain kernel's.
+// whole prompt would.  The keys of query tile qt's rows (128 qt .. 128 qt +
+// 127) are its unit's last four sub-tiles; the workgroup of the first query
+// head of each KV group (g = 0) stores the rows of them that the ring keeps,
+// after its loop, staging each such sub-tile once more (the loop has just
+// read it, so it comes from L2).  Every ring row is therefore written once.
+// The loop itself is the plain kernel's, so o is bit-identical to it.  The
+// f32 kernel stores the same rows from its tile loop.
 
 #include "moa_device.h"
 #include "moa_internal.h"
@@ -67,19 +69,24 @@ namespace {
 constexpr int BM = kPrefillBM;
 constexpr int BN = kPrefillBN;
 
-// LDS layout of a 64-row K or V tile (row = key): 16-byte chunks (8 dims)
-// in groups of four; group cg holds its 64-byte slice of all 64 rows, and
-// the chunk's place inside the slice is XOR-swizzled by row bits 2-3.  Byte
-// offset of chunk c of row r:
+// The bf16 kernel streams each 64-key tile of the plan as two 32-key
+// sub-tiles, so that a workgroup needs 32 KB of LDS and 166 VGPRs a lane, and
+// three workgroups (three waves a SIMD) share a CU.
+constexpr int BS = 32;
+
+// LDS layout of a 32-row K or V sub-tile (row = key): 16-byte chunks (8
+// dims) in groups of four; group cg holds its 64-byte slice of all 32 rows,
+// and the chunk's place inside the slice is XOR-swizzled by row bits 2-3.
+// Byte offset of chunk c of row r:
 __device__ __forceinline__ constexpr int tile_off(int r, int c) {
-  return (c >> 2) * 4096 + r * 64 + (((c & 3) ^ ((r >> 2) & 3)) << 4);
+  return (c >> 2) * 2048 + r * 64 + (((c & 3) ^ ((r >> 2) & 3)) << 4);
 }
 // (One wave's 16-byte LDS-direct load fills 1 KB: 16 rows of one group.
 // The 16 lanes of an LDS read phase meet 16 different rows of one chunk
 // column in different banks, for the K reads and the transposed V reads.)
 
 template <int D, bool RING>
-__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
+__global__ __launch_bounds__(256, 3) void prefill_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, const int4* __restrict__ items, const int32_t* __restrict__ span,
     const int32_t* __restrict__ seq_len, int seq_grid, int Hq, int Hkv, int G, int Npad,
@@ -88,10 +95,12 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
   constexpr int KS = D / 16;       // k-steps of the Q.K product
   constexpr int OT = D / 32;       // 32-dim tiles of the output
   constexpr int ROWB = D * 2;      // bytes of a K/V row
-  constexpr int TILEB = BN * ROWB; // bytes of a K or V tile
-  constexpr int NDMA = D / 32;     // LDS-direct rounds per tile (chunk groups)
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][BN * D];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2][BN * D];
+  constexpr int TILEB = BS * ROWB; // bytes of a K or V sub-tile
+  constexpr int NDMA = D / 64;     // LDS-direct rounds per sub-tile
+  constexpr int TE = BS * D;       // elements of a sub-tile
+  // sub-tile buffers: K in 0 and 1, V in 2 and 3 (one array, so that the O
+  // epilogue can stage all four waves' rows in it)
+  __shared__ __attribute__((aligned(16))) bf16 lds[4 * TE];
 
   const int tid = threadIdx.x;
   // wave-uniform, so that the LDS addresses of the tile loads are scalar
@@ -128,30 +137,38 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
     }
   }
 
-  // LDS-direct staging: round i of wave w fills bytes i*4096 + w*1024 +
-  // 16*lane of a tile, i.e. chunk group i, rows 16w + lane/4, slice place
-  // lane % 4, which holds chunk 4i + ((lane % 4) ^ (lane / 16 % 4)) of that
-  // row.  Rows at or past N read as zero (buffer bounds).
+  // LDS-direct staging: round i of wave w fills bytes g*2048 + (w%2)*1024 +
+  // 16*lane of a sub-tile, g = 2i + w/2: chunk group g, rows 16(w%2) +
+  // lane/4, slice place lane % 4, which holds chunk 4g + ((lane % 4) ^
+  // (lane / 16 % 4)) of that row.  Rows at or past N read as zero (buffer
+  // bounds).
   const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(kb, (uint32_t)N * ROWB);
   const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(vb, (uint32_t)N * ROWB);
-  const uint32_t dma_off =
-      (uint32_t)(16 * wave + (lane >> 2)) * ROWB + (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) << 4);
+  const uint32_t dma_off = (uint32_t)(16 * (wave & 1) + (lane >> 2)) * ROWB +
+                           (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) << 4);
   // The loads are issued from inline assembly so that the compiler, which
   // cannot tell that they fill the other buffer, does not wait for them
   // before every LDS read of the current one; the explicit vmcnt(0) before
   // each barrier is their only wait.  They write no registers.
-  auto dma_tile = [&](int kt, int buf) {
+  auto dma_tile = [&](int st, int buf) {
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) {
-      const uint32_t soff = (uint32_t)kt * TILEB + i * 64;
-      const int dst = i * 4096 + wave * 1024;
-      lds_direct_ld16(krs, dma_off, soff, (char*)&Ks[buf][0] + dst);
-      lds_direct_ld16(vrs, dma_off, soff, (char*)&Vs[buf][0] + dst);
+      const int grp = 2 * i + (wave >> 1);
+      const uint32_t soff = (uint32_t)st * TILEB + grp * 64;
+      const int dst = grp * 2048 + (wave & 1) * 1024;
+      lds_direct_ld16(krs, dma_off, soff, (char*)&lds[buf * TE] + dst);
+      lds_direct_ld16(vrs, dma_off, soff, (char*)&lds[(2 + buf) * TE] + dst);
     }
   };
 
-  // the first tile's loads go out before Q's, so their latencies overlap
-  dma_tile(kt_lo, 0);
+  // The unit's sub-tiles: those of its 64-key tiles, less a leading one that
+  // no row of the unit keeps.
+  const int lo_key = qt * BM - S + 1;
+  int st_lo = 2 * kt_lo;
+  if (lo_key > 0 && lo_key / BS > st_lo) st_lo = lo_key / BS;
+  const int st_hi = 2 * kt_hi + 1;
+  // the first sub-tile's loads go out before Q's, so their latencies overlap
+  dma_tile(st_lo, 0);
 
   const int iw0 = qt * BM + wave * 32;  // first query row of this wave
   const int my_q = iw0 + l32;
@@ -182,9 +199,9 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
 #pragma unroll
   for (int r = 0; r < 16; ++r) minit[r] = 0.f;
 
-  // K fragment (Q.K, tile t, k-step s): row 32t + kperm, chunk 2s + half.
-  // With kperm's row bits 2-3 fixed per lane, the byte offset is a per-lane
-  // base (one for even s, one for odd s) plus (s / 2) * 4096 + t * 2048.
+  // K fragment (Q.K k-step s): row kperm, chunk 2s + half.  With kperm's row
+  // bits 2-3 fixed per lane, the byte offset is a per-lane base (one for even
+  // s, one for odd s) plus (s / 2) * 2048.
   const int kperm = 16 * (l32 >> 4) + 8 * ((l32 >> 2) & 1) + 4 * ((l32 >> 3) & 1) + (l32 & 3);
   const int kx = (kperm >> 2) & 3;
   const int k_even = kperm * 64 + ((half ^ kx) << 4);
@@ -198,108 +215,52 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
   const int v_rd0 = v_lane + ((v_c ^ ((2 * (vg >> 1)) & 3)) << 4);
   const int v_rd1 = v_lane + ((v_c ^ ((2 * (vg >> 1) + 1) & 3)) << 4);
 
-  // Fused handoff: the tile's rows that the ring keeps (positions N - S ..
-  // N - 1, slot p mod S) go from LDS to the rings.  K: 16-byte chunks.  V:
-  // transposed reads give 4 consecutive keys of one dimension, stored as one
-  // 8-byte run when the 4 slots are consecutive (S a multiple of 4, or S = N:
-  // slot = p), else element by element.
-  auto ring_tile = [&](int kt, int buf) {
-    if constexpr (RING) {
-      if (kring == nullptr || kt * BN / BM != qt || (kt + 1) * BN <= N - S) return;
-      const char* kl = (const char*)&Ks[buf][0];
-      const char* vl = (const char*)&Vs[buf][0];
-      constexpr int CPR = D / 8;
-#pragma unroll
-      for (int u = 0; u < CPR / 4; ++u) {
-        const int id = u * 256 + tid;
-        const int r = id / CPR, c = id % CPR;
-        const int p = kt * BN + r;
-        if (p >= N - S && p < N)
-          st16(kring + (int64_t)(p % S) * D + 8 * c, *reinterpret_cast<const bf16x8*>(kl + tile_off(r, c)));
-      }
-      // 16 key groups x D/16 dim blocks, one per 16-lane group and round
-      const int grp = tid >> 4;
-#pragma unroll
-      for (int u = 0; u < D / 16; ++u) {
-        const int unit = u * 16 + grp;
-        const int kg = unit & 15, m = unit >> 4;
-        const int r = 4 * kg + (vi >> 2);
-        const int dim0 = 16 * m + 4 * (vi & 3);
-        const int off = tile_off(r, dim0 >> 3) + 2 * (dim0 & 7);
-        const bf16x4 x = lds_read_tr16(vl + off);
-        const int p0 = kt * BN + 4 * kg;
-        const int d = 16 * m + vi;
-        if (p0 >= N - S && p0 + 3 < N && (S % 4 == 0 || S == N)) {
-          const int slot0 = p0 % S;
-          *reinterpret_cast<bf16x4*>(vring + (int64_t)(slot0 >> 5) * (32 * D) + d * 32 + (slot0 & 31)) = x;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int p = p0 + e;
-            if (p >= N - S && p < N) {
-              const int slot = p % S;
-              vring[(int64_t)(slot >> 5) * (32 * D) + d * 32 + (slot & 31)] = x[e];
-            }
-          }
-        }
-      }
-    }
-  };
-
-  // Double-buffered LDS-direct tiles: tile kt+1's loads are issued before
-  // tile kt is computed; one wait and one barrier a tile.
+  // Double-buffered LDS-direct sub-tiles: sub-tile st+1's loads are issued
+  // before sub-tile st is computed; one wait and one barrier a sub-tile.
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
-  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-    const int buf = (kt - kt_lo) & 1;
-    if (kt < kt_hi) dma_tile(kt + 1, buf ^ 1);
+  for (int st = st_lo; st <= st_hi; ++st) {
+    const int buf = (st - st_lo) & 1;
+    if (st < st_hi) dma_tile(st + 1, buf ^ 1);
 
-    const int j0 = kt * BN;
-    const bool active = iw0 < N && j0 <= iw0 + 31 && j0 + BN - 1 >= iw0 - S + 1;
+    const int j0 = st * BS;
+    const bool active = iw0 < N && j0 <= iw0 + 31 && j0 + BS - 1 >= iw0 - S + 1;
     if (active) {
-      const bool full = j0 + BN - 1 <= iw0 && j0 >= iw0 + 31 - S + 1 && j0 + BN <= N;
-      const char* kl = (const char*)&Ks[buf][0];
-      const char* vl = (const char*)&Vs[buf][0];
-      floatx16 st[2];
+      const bool full = j0 + BS - 1 <= iw0 && j0 >= iw0 + 31 - S + 1 && j0 + BS <= N;
+      const char* kl = (const char*)&lds[buf * TE];
+      const char* vl = (const char*)&lds[(2 + buf) * TE];
+      floatx16 sc = minit;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        st[t] = minit;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const int off = ((s & 1) ? k_odd : k_even) + (s >> 1) * 4096 + t * 2048;
-          st[t] = mfma32(*reinterpret_cast<const bf16x8*>(kl + off), qop[s], st[t]);
-        }
+      for (int s = 0; s < KS; ++s) {
+        const int off = ((s & 1) ? k_odd : k_even) + (s >> 1) * 2048;
+        sc = mfma32(*reinterpret_cast<const bf16x8*>(kl + off), qop[s], sc);
       }
       // keep four K-fragment reads in flight ahead of the matrix cores
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-      for (int i = 0; i < 2 * KS - 4; ++i) {
+      for (int i = 0; i < KS - 4; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      // st[t][r] is raw score - m_ref of query my_q and key
-      // j0 + 32t + 16(r>>3) + 8half + (r&7)
+      // sc[r] is raw score - m_ref of query my_q and key
+      // j0 + 16(r>>3) + 8half + (r&7)
       if (!full) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = j0 + 32 * t + 16 * (r >> 3) + 8 * half + (r & 7);
-            const bool ok = key <= my_q && key >= my_q - S + 1 && key < N;
-            st[t][r] = ok ? st[t][r] : -INFINITY;
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int key = j0 + 16 * (r >> 3) + 8 * half + (r & 7);
+          const bool ok = key <= my_q && key >= my_q - S + 1 && key < N;
+          sc[r] = ok ? sc[r] : -INFINITY;
+        }
       }
-      float mx = st[0][0];
+      float mx = sc[0];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[t][r]);
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
       mx = half_swap_max(mx);
       // Lazy rescale: the reference moves (and O, l are rescaled) only when
-      // some row's tile max exceeds it by more than 8 in the exp2 domain, or
-      // sets it at the row's first kept key; otherwise p <= 256, harmless in
-      // fp32 and bf16.  The final O / l is unchanged.
+      // some row's sub-tile max exceeds it by more than 8 in the exp2 domain,
+      // or sets it at the row's first kept key; otherwise p <= 256, harmless
+      // in fp32 and bf16.  The final O / l is unchanged.
       if (__ballot(mx > thr || (m_run == -INFINITY && mx != -INFINITY))) {
         const float m_new = fmaxf(m_run, mx == -INFINITY ? -INFINITY : m_ref + mx);
         const bool set = m_new != -INFINITY;   // else: no kept key yet, nothing moves
@@ -313,19 +274,16 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
         l_b *= alpha;
 #pragma unroll
         for (int t = 0; t < OT; ++t) acc[t] *= alpha;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) st[t] -= delta;
+        sc -= delta;
 #pragma unroll
         for (int r = 0; r < 16; ++r) minit[r] = -m_ref;
       }
-      float p[2][16];
+      float p[16];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int r = 0; r < 16; ++r) p[r] = fast_exp2(sc[r] * scale_log2);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) p[t][r] = fast_exp2(st[t][r] * scale_log2);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x8 pop = to_bf16x8(&p[j >> 1][8 * (j & 1)]);
+      for (int j = 0; j < 2; ++j) {
+        const bf16x8 pop = to_bf16x8(&p[8 * j]);
         // the row sum of the bf16 weights the P.V product uses, two per step
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -335,7 +293,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
         }
 #pragma unroll
         for (int t = 0; t < OT; ++t) {
-          const int base = t * 4096 + 16 * j * 64;
+          const int base = t * 2048 + 16 * j * 64;
           const bf16x4 a0 = lds_read_tr16(vl + base + v_rd0);
           const bf16x4 a1 = lds_read_tr16(vl + base + 4 * 64 + v_rd1);
           const bf16x8 vop = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -345,33 +303,83 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
       // same for the V^T fragments of the P.V product
       __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
 #pragma unroll
-      for (int i = 0; i < 4 * OT - 4; ++i) {
+      for (int i = 0; i < 2 * OT - 4; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): tile kt+1 is in LDS
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): sub-tile st+1 is in LDS
     __syncthreads();
   }
 
   if constexpr (RING) {
-    // The ring keeps rows of the unit's diagonal key tiles (2 qt and 2 qt + 1),
-    // the loop's last one or two tiles, which are still in their buffers.
-    if (kt_hi - 1 >= kt_lo) ring_tile(kt_hi - 1, (kt_hi - 1 - kt_lo) & 1);
-    ring_tile(kt_hi, (kt_hi - kt_lo) & 1);
-    __syncthreads();   // before O is staged in the K buffers
+    // Fused handoff: the ring keeps positions N - S .. N - 1 at slot p mod
+    // S.  Each key sub-tile's ring rows are written by the unit of its query
+    // tile (the unit's last four sub-tiles, 4 qt .. 4 qt + 3), after the
+    // loop: each such sub-tile is staged again (from L2, where the loop just
+    // read it) into buffers 0 and 2 and copied out.  K: 16-byte chunks.  V:
+    // transposed reads give 4 consecutive keys of one dimension, stored as
+    // one 8-byte run when the 4 slots are consecutive (S a multiple of 4, or
+    // S = N: slot = p), else element by element.
+    if (kring != nullptr) {
+      constexpr int CPR = D / 8;
+      const char* kl = (const char*)&lds[0];
+      const char* vl = (const char*)&lds[2 * TE];
+      const int grp = tid >> 4;
+      for (int st = 4 * qt; st <= st_hi; ++st) {
+        if ((st + 1) * BS <= N - S || st * BS >= N) continue;   // no row of it is kept
+        dma_tile(st, 0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0)
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < CPR / 8; ++u) {
+          const int id = u * 256 + tid;
+          const int r = id / CPR, c = id % CPR;
+          const int p = st * BS + r;
+          if (p >= N - S && p < N)
+            st16(kring + (int64_t)(p % S) * D + 8 * c,
+                 *reinterpret_cast<const bf16x8*>(kl + tile_off(r, c)));
+        }
+        // 8 key groups x D/16 dim blocks, one per 16-lane group and round
+#pragma unroll
+        for (int u = 0; u < D / 32; ++u) {
+          const int unit = u * 16 + grp;
+          const int kg = unit & 7, m = unit >> 3;
+          const int r = 4 * kg + (vi >> 2);
+          const int dim0 = 16 * m + 4 * (vi & 3);
+          const int off = tile_off(r, dim0 >> 3) + 2 * (dim0 & 7);
+          const bf16x4 x = lds_read_tr16(vl + off);
+          const int p0 = st * BS + 4 * kg;
+          const int d = 16 * m + vi;
+          if (p0 >= N - S && p0 + 3 < N && (S % 4 == 0 || S == N)) {
+            const int slot0 = p0 % S;
+            *reinterpret_cast<bf16x4*>(vring + (int64_t)(slot0 >> 5) * (32 * D) + d * 32 + (slot0 & 31)) = x;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int p = p0 + e;
+              if (p >= N - S && p < N) {
+                const int slot = p % S;
+                vring[(int64_t)(slot >> 5) * (32 * D) + d * 32 + (slot & 31)] = x[e];
+              }
+            }
+          }
+        }
+        __syncthreads();   // before the buffers are filled again
+      }
+    }
   }
 
-  // O through LDS: each wave writes its 32 normalised rows into its own part
-  // of the (now idle) K buffers, chunk c of row r at byte
+  // O through LDS: each wave writes its 32 normalised rows into its own
+  // quarter of the (now idle) sub-tile buffers, chunk c of row r at byte
   // 16 * (c ^ (r mod chunks per row)), and reads them back as whole 16-byte
   // chunks, so that each store instruction writes four complete output rows.
   // Rows at or past N are not stored.
   const float l_run = half_swap_sum(l_a + l_b);
   const float inv = 1.f / l_run;
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
-  char* ow = (char*)&Ks[0][0] + wave * (32 * D * 2);
+  char* ow = (char*)&lds[0] + wave * (32 * D * 2);
 #pragma unroll
   for (int t = 0; t < OT; ++t)
 #pragma unroll
