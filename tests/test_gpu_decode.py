@@ -57,6 +57,9 @@ CASES = [
     # rings of exactly one and two 1024-slot chunks
     (1, 4, 2, 128, 1024, [1024, 0], [0.0, 0.5], 3),
     (1, 2, 2, 128, 2048, [0, 0], [1.0, 0.5], 3),
+    # the largest group the boundary takes (G = 16), multi-chunk rings, D 128 and 64
+    (2, 16, 1, 128, 1500, [0], [0.6], 3),
+    (1, 32, 2, 64, 2100, [0, 1100], [0.5, 0.0], 3),
 ]
 
 

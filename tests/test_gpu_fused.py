@@ -96,6 +96,8 @@ APPEND_CASES = [
     (1, 8, 2, 64, 3100, [2048, 0], [0.0, 0.4], 3),
     # more steps than either span (64 and 100): every slot rewritten by decode tokens
     (2, 4, 2, 128, 100, [64, 0], [0.0, 1.0], 150),
+    # the largest group the boundary takes (G = 16)
+    (1, 16, 1, 128, 2200, [0], [0.9], 3),
 ]
 
 

@@ -57,6 +57,9 @@ CASES = [
     (2, 4, 4, 128, 65, [0, 64, 1, 0], [0.5, 0.0, 0.0, 1.0], "bf16"),
     (1, 4, 2, 128, 256, [128, 0], [0.0, 0.5], "bf16"),
     (2, 4, 2, 64, 333, [0, 200], [0.5, 0.0], "f32"),
+    # the largest group the boundary takes (G = 16), both dtypes
+    (1, 16, 1, 128, 700, [0], [0.5], "bf16"),
+    (1, 32, 2, 64, 300, [0, 100], [0.4, 0.0], "f32"),
     (1, 2, 2, 128, 257, [0, 64], [1.0, 0.0], "f32"),
 ]
 
