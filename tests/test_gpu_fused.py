@@ -58,6 +58,9 @@ HANDOFF_CASES = [
     (3, 6, 3, 128, 2049, [0, 64, 2000], [1.0, 0.0, 0.0], "bf16"),
     (2, 4, 2, 64, 333, [0, 200], [0.5, 0.0], "f32"),
     (1, 2, 2, 128, 257, [0, 64], [1.0, 0.0], "f32"),
+    # the largest group the boundary takes (G = 16): one handoff per KV group
+    (1, 16, 1, 128, 700, [0], [0.5], "bf16"),
+    (1, 32, 2, 64, 300, [0, 100], [0.4, 0.0], "f32"),
 ]
 
 
