@@ -1,9 +1,11 @@
-"""The decode planner's dispatch model assumes a number of resident decode workgroups per CU
+"""Occupancies the design relies on, checked against what the compiler reaches.
+
+The decode planner's dispatch model assumes a number of resident decode workgroups per CU
 for each head dimension (kDecodeResidentD64, kDecodeResidentD128 in csrc/moa_internal.h).
 They must equal the occupancy the compiled decode kernels reach: the compiler reports it for
 each kernel, in waves per SIMD, and a 256-thread workgroup puts one wave on each SIMD of a CU.
-Checked on the gfx950 assembly of decode.hip built with the build's flags (no GPU needed;
-skipped without hipcc)."""
+The bf16 prefill kernel is laid out for three workgroups per CU. Checked on the gfx950
+assembly of the sources built with the build's flags (no GPU needed; skipped without hipcc)."""
 
 import importlib.util
 import os
@@ -47,3 +49,29 @@ def test_decode_residency_matches_compiled_occupancy(tmp_path):
     assert set(found) == {(64, "0"), (64, "1"), (128, "0"), (128, "1")}, found
     for (d, _), occ in found.items():
         assert occ == want[d], (d, occ, want[d])
+
+
+def test_prefill_runs_three_workgroups_per_cu(tmp_path):
+    """The bf16 prefill kernel is laid out for three 256-thread workgroups per CU (32 KB of LDS
+    and at most 168 VGPRs each: three waves on every SIMD), and its launch bounds ask for that.
+    The plain and the fused-handoff kernels of both head dims must reach it: a source change
+    that pushes the register count past 168 would silently drop it from three waves per SIMD
+    to two."""
+    b = _build_module()
+    try:
+        b.hipcc()
+    except RuntimeError:
+        pytest.skip("hipcc not available")
+    out = str(tmp_path / "prefill.s")
+    cmd = [b.hipcc(), *b.COMMON, *b.EXTRA.get("prefill.hip", []), "-x", "hip",
+           "--cuda-device-only", "-S", os.path.join(b.CSRC, "prefill.hip"), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    asm = open(out).read()
+    found = {}
+    for m in re.finditer(r"^(_Z\S*prefill_bf16_kernelILi(\d+)ELb([01])E\S*):", asm, re.M):
+        occ = re.compile(r"^; Occupancy: (\d+)", re.M).search(asm, m.end())
+        found[(int(m.group(2)), m.group(3))] = int(occ.group(1))
+    assert set(found) == {(64, "0"), (64, "1"), (128, "0"), (128, "1")}, found
+    for key, occ in found.items():
+        assert occ >= 3, (key, occ)
