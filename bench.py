@@ -189,7 +189,7 @@ def run_decode(moa, workloads, torch, name, steps, warmup, dense=False):
 
 
 def run_prefill(moa, workloads, torch, name, iters, warmup, dense=False, warmup_ms=0.0):
-    """Median prefill time, and the prompt's handoff to the rings both ways: a separate
+    """Mean prefill time per call, and the prompt's handoff to the rings both ways: a separate
     moa_kv_append(pos0 = 0, n_new = N) and the fused moa_prefill_handoff.
 
     Before each of the two timed runs (plain, fused), the same call runs `warmup` times and
@@ -221,7 +221,7 @@ def run_prefill(moa, workloads, torch, name, iters, warmup, dense=False, warmup_
             fn()
             b.record(stream)
         torch.cuda.synchronize()
-        return float(np.median([a.elapsed_time(b) for a, b in ev]))
+        return float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
     def warm(fn):
         t0 = time.perf_counter()
