@@ -2,7 +2,8 @@
 
 Each case draws its own shape from a seeded PCG64 stream:
 - batch 1-4, 1-4 KV heads of group size 1, 2 or 4, head dim 64 or 128, and a prompt of
-  1-700 tokens;
+  1-700 tokens; or, in the wide-group cases, batch 1-2, 1-2 KV heads of group size 8 or 16
+  and a prompt of 700-1500 tokens;
 - a uniform or a left-padded ragged batch (NaN in the padding rows);
 - rules with non-dyadic beta, and alpha up to past N;
 - bf16 for most cases, fp32 for every fourth.
@@ -31,19 +32,27 @@ pytestmark = pytest.mark.gpu
 TOL = {"f32": 1e-4, "bf16": 2e-2}
 _BITS = {torch.bfloat16: torch.int16, torch.float32: torch.int32}
 N_CASES = int(os.environ.get("MOA_RANDOM_CASES", "24"))   # more for an extended run
+N_WIDE = int(os.environ.get("MOA_RANDOM_WIDE_CASES", "8"))
 
 
 def _bits(t):
     return t.contiguous().view(_BITS[t.dtype]).numpy()
 
 
-def _case(i):
-    rng = np.random.Generator(np.random.PCG64(4242 + i))
-    hkv = int(rng.integers(1, 5))
-    g = int(rng.choice([1, 2, 4]))
-    d = int(rng.choice([64, 128]))
-    bsz = int(rng.integers(1, 5))
-    n = int(rng.integers(1, 701))
+def _case(i, wide=False):
+    rng = np.random.Generator(np.random.PCG64((7373 if wide else 4242) + i))
+    if wide:    # wide groups, longer prompts
+        hkv = int(rng.integers(1, 3))
+        g = int(rng.choice([8, 16]))
+        d = int(rng.choice([64, 128]))
+        bsz = int(rng.integers(1, 3))
+        n = int(rng.integers(700, 1501))
+    else:
+        hkv = int(rng.integers(1, 5))
+        g = int(rng.choice([1, 2, 4]))
+        d = int(rng.choice([64, 128]))
+        bsz = int(rng.integers(1, 5))
+        n = int(rng.integers(1, 701))
     dt = "f32" if i % 4 == 3 else "bf16"
     lens = None
     if bsz > 1 and rng.integers(0, 2):
@@ -70,7 +79,15 @@ def _check_rings(lay, kc, vc, hist_k, hist_v, done):
 
 @pytest.mark.parametrize("case", range(N_CASES))
 def test_random_configuration(moa, case):
-    bsz, hq, hkv, d, n, lens, alpha, beta, dt = _case(case)
+    _run_case(moa, case, *_case(case))
+
+
+@pytest.mark.parametrize("case", range(N_WIDE))
+def test_random_configuration_wide_groups(moa, case):
+    _run_case(moa, case, *_case(case, wide=True))
+
+
+def _run_case(moa, case, bsz, hq, hkv, d, n, lens, alpha, beta, dt):
     log(f"random case {case}: B{bsz} Hq{hq} Hkv{hkv} D{d} N{n} lens {lens} {dt} "
         f"alpha {alpha} beta {[round(x, 4) for x in beta]}")
     plan = moa.Plan(bsz, hq, hkv, d, n, alpha, beta, dtype=dt, seq_len=lens)
